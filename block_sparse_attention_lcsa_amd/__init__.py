@@ -1,0 +1,263 @@
+"""Python binding of liblcsa (LCSA select + block-sparse attention on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of liblcsa.so.
+torch supplies device memory and the current stream.  If the library is not
+built the import fails; there is no other code path.
+
+    import block_sparse_attention_lcsa_amd as lcsa
+    plan = lcsa.Plan(batch=1, heads=12, head_dim=128, grid_h=48, grid_w=80,
+                     q_frames=6, kv_ratio=3.0, local_range=11, topk_ratio=2.0)
+    row_ptr, col_idx = lcsa.select(plan, q, k)
+    o = lcsa.attend(plan, q, k, v, row_ptr, col_idx)
+
+q, k, v are bf16 CUDA(HIP) tensors of shape [batch, tokens, heads, 128] in
+raster token order; any strides with a contiguous last dimension.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["Plan", "LcsaError", "select", "attend", "lib_path", "abi_version", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "liblcsa.so")
+
+
+if not os.path.exists(lib_path()):
+    raise ImportError(
+        "liblcsa.so is not built; run `python -m block_sparse_attention_lcsa_amd.build_lib` "
+        "(hipcc, gfx950). There is no fallback implementation.")
+
+_lib = ctypes.CDLL(lib_path())
+
+# Every symbol include/lcsa.h declares.
+EXPORTS = [
+    "lcsa_plan_create", "lcsa_plan_destroy", "lcsa_plan_get_info", "lcsa_plan_row_ptr",
+    "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_status_string",
+    "lcsa_last_error", "lcsa_abi_version",
+]
+
+LCSA_DTYPE_BF16 = 1
+STATUS = {0: "LCSA_OK", 1: "LCSA_ERR_NULL", 2: "LCSA_ERR_INVALID", 3: "LCSA_ERR_SHAPE",
+          4: "LCSA_ERR_ALIGN", 5: "LCSA_ERR_WORKSPACE", 6: "LCSA_ERR_DEVICE",
+          7: "LCSA_ERR_LAUNCH", 8: "LCSA_ERR_INTERNAL"}
+
+
+class LcsaDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("q_frames", ctypes.c_int32),
+                ("cached_frames", ctypes.c_int32), ("block_t", ctypes.c_int32),
+                ("block_h", ctypes.c_int32), ("block_w", ctypes.c_int32),
+                ("local_range", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("topk_ratio", ctypes.c_double), ("kv_ratio", ctypes.c_float),
+                ("scale", ctypes.c_float)]
+
+
+class LcsaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class LcsaPlanInfo(ctypes.Structure):
+    _fields_ = [("kv_frames", ctypes.c_int32), ("blocks_per_frame", ctypes.c_int32),
+                ("nbh", ctypes.c_int32), ("nbw", ctypes.c_int32), ("nqb", ctypes.c_int32),
+                ("nkb", ctypes.c_int32), ("k", ctypes.c_int32), ("block_h", ctypes.c_int32),
+                ("block_w", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
+                ("half_window", ctypes.c_int32), ("max_row_nnz", ctypes.c_int32),
+                ("min_window", ctypes.c_int32), ("max_window", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("q_tokens", ctypes.c_int64), ("kv_tokens", ctypes.c_int64),
+                ("select_workspace_bytes", ctypes.c_uint64), ("scale", ctypes.c_double),
+                ("useful_flops", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_lib.lcsa_plan_create.argtypes = [ctypes.POINTER(LcsaDesc), ctypes.POINTER(_P)]
+_lib.lcsa_plan_create.restype = ctypes.c_int32
+_lib.lcsa_plan_destroy.argtypes = [_P]
+_lib.lcsa_plan_destroy.restype = None
+_lib.lcsa_plan_get_info.argtypes = [_P, ctypes.POINTER(LcsaPlanInfo)]
+_lib.lcsa_plan_get_info.restype = ctypes.c_int32
+_lib.lcsa_plan_row_ptr.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64]
+_lib.lcsa_plan_row_ptr.restype = ctypes.c_int32
+_lib.lcsa_plan_window.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+_lib.lcsa_plan_window.restype = ctypes.c_int32
+_lib.lcsa_select.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                             _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lcsa_select.restype = ctypes.c_int32
+_lib.lcsa_attend.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                             ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_int64,
+                             ctypes.POINTER(LcsaTensor), _P, _P]
+_lib.lcsa_attend.restype = ctypes.c_int32
+_lib.lcsa_status_string.argtypes = [ctypes.c_int32]
+_lib.lcsa_status_string.restype = ctypes.c_char_p
+_lib.lcsa_last_error.argtypes = []
+_lib.lcsa_last_error.restype = ctypes.c_char_p
+_lib.lcsa_abi_version.argtypes = []
+_lib.lcsa_abi_version.restype = ctypes.c_int32
+
+
+class LcsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        detail = _lib.lcsa_last_error().decode()
+        super().__init__(f"{where}: {self.name}: {detail}")
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise LcsaError(st, where)
+
+
+def abi_version() -> int:
+    return _lib.lcsa_abi_version()
+
+
+class Plan:
+    """Host-side plan of one LCSA layer shape (no GPU needed)."""
+
+    def __init__(self, batch, heads, grid_h, grid_w, q_frames, head_dim=128, cached_frames=0,
+                 kv_ratio=3.0, block_t=0, block_h=0, block_w=0, local_range=11,
+                 topk_ratio=0.0, topk=0, scale=0.0):
+        d = LcsaDesc(batch=batch, heads=heads, head_dim=head_dim, grid_h=grid_h, grid_w=grid_w,
+                     q_frames=q_frames, cached_frames=cached_frames, block_t=block_t,
+                     block_h=block_h, block_w=block_w, local_range=local_range, topk=topk,
+                     topk_ratio=topk_ratio, kv_ratio=kv_ratio, scale=scale)
+        h = _P()
+        _check(_lib.lcsa_plan_create(ctypes.byref(d), ctypes.byref(h)), "lcsa_plan_create")
+        self._h = h
+        self.desc = {f: getattr(d, f) for f, _ in LcsaDesc._fields_}
+        inf = LcsaPlanInfo()
+        _check(_lib.lcsa_plan_get_info(h, ctypes.byref(inf)), "lcsa_plan_get_info")
+        self.info = {f: getattr(inf, f) for f, _ in LcsaPlanInfo._fields_}
+
+    @classmethod
+    def from_desc(cls, desc: dict) -> "Plan":
+        return cls(**{k: v for k, v in desc.items()})
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.lcsa_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def row_ptr(self):
+        import numpy as np
+        n = self.info["rows"] + 1
+        out = np.zeros(n, dtype=np.int32)
+        _check(_lib.lcsa_plan_row_ptr(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n),
+               "lcsa_plan_row_ptr")
+        return out
+
+    def window(self, qb: int):
+        import numpy as np
+        cap = self.info["max_window"]
+        out = np.zeros(max(cap, 1), dtype=np.int32)
+        cnt = ctypes.c_int32()
+        _check(_lib.lcsa_plan_window(self._h, qb, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     len(out), ctypes.byref(cnt)), "lcsa_plan_window")
+        return out[:cnt.value]
+
+
+def tensor_view(t) -> LcsaTensor:
+    """lcsa_tensor of a [B, S, H, D] bf16 torch tensor (contiguous last dim)."""
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"expected bfloat16, got {t.dtype}")
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [batch, tokens, heads, head_dim] view with contiguous last dim")
+    sb, ss, sh, _ = t.stride()
+    return LcsaTensor(data=t.data_ptr(), dtype=LCSA_DTYPE_BF16, reserved=0,
+                      stride_b=sb, stride_s=ss, stride_h=sh)
+
+
+def _check_shape(t, plan: Plan, tokens_key: str, name: str):
+    inf, d = plan.info, plan.desc
+    want = (d["batch"], inf[tokens_key], d["heads"], d["head_dim"])
+    if tuple(t.shape) != want:
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {want}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def _stream_ptr(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream
+
+
+def select(plan: Plan, q, k, return_scores: bool = False, workspace=None, stream=None):
+    """Top-k block selection.  Returns (row_ptr int32 [rows+1], col_idx int32
+    [nnz]) and, with return_scores, the float64 pooled scores
+    [B, H, NQB, NKB] (-inf outside the window)."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_shape(k, plan, "kv_tokens", "k")
+    inf = plan.info
+    dev = q.device
+    row_ptr = torch.empty(inf["rows"] + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(inf["nnz"], 1), dtype=torch.int32, device=dev)[: inf["nnz"]]
+    ws_bytes = int(inf["select_workspace_bytes"])
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scores = None
+    if return_scores:
+        d = plan.desc
+        scores = torch.empty((d["batch"], d["heads"], inf["nqb"], inf["nkb"]),
+                             dtype=torch.float64, device=dev)
+    qv, kv = tensor_view(q), tensor_view(k)
+    st = _lib.lcsa_select(plan.handle, ctypes.byref(qv), ctypes.byref(kv),
+                          row_ptr.data_ptr(), col_idx.data_ptr() if inf["nnz"] else None,
+                          scores.data_ptr() if scores is not None else None,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_ptr(q, stream))
+    _check(st, "lcsa_select")
+    if return_scores:
+        return row_ptr, col_idx, scores
+    return row_ptr, col_idx
+
+
+def attend(plan: Plan, q, k, v, row_ptr, col_idx, out=None, return_lse: bool = False,
+           stream=None):
+    """Block-sparse attention forward over the CSR (row_ptr, col_idx)."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_shape(k, plan, "kv_tokens", "k")
+    _check_shape(v, plan, "kv_tokens", "v")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != plan.info["rows"] + 1 or not row_ptr.is_contiguous():
+        raise ValueError("row_ptr must hold rows + 1 contiguous int32")
+    if not col_idx.is_contiguous():
+        raise ValueError("col_idx must be contiguous")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    else:
+        _check_shape(out, plan, "q_tokens", "out")
+    lse = None
+    if return_lse:
+        d = plan.desc
+        lse = torch.empty((d["batch"], d["heads"], plan.info["q_tokens"]), dtype=torch.float32,
+                          device=q.device)
+    qv, kv, vv, ov = tensor_view(q), tensor_view(k), tensor_view(v), tensor_view(out)
+    st = _lib.lcsa_attend(plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
+                          row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else None,
+                          col_idx.numel(), ctypes.byref(ov),
+                          lse.data_ptr() if lse is not None else None, _stream_ptr(q, stream))
+    _check(st, "lcsa_attend")
+    if return_lse:
+        return out, lse
+    return out

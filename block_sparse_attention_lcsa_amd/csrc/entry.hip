@@ -1,0 +1,174 @@
+// C-ABI entry points lcsa_select and lcsa_attend: validate on the host, then
+// enqueue the kernels on the caller's stream.  Nothing is enqueued when a
+// check fails, and there is no alternative code path (the FlashVSR+ README,
+// "Install an attention backend", and the FlashVSR Inference skill page,
+// "Backend Gate", both make an unavailable sparse kernel an error rather than
+// a silent dense fallback).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "kernel_params.h"
+#include "launch.h"
+#include "lcsa_internal.h"
+
+namespace lcsa {
+namespace {
+
+lcsa_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(LCSA_ERR_DEVICE, "no current HIP device");
+  static std::mutex mu;
+  static signed char known[256] = {0};  // 0 unknown, 1 gfx950, -1 other
+  if (dev >= 256) return fail(LCSA_ERR_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(LCSA_ERR_DEVICE, "cannot query device %d", dev);
+    known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (known[dev] < 0)
+      return fail(LCSA_ERR_DEVICE, "device %d is %s; liblcsa is built for gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  return known[dev] > 0 ? LCSA_OK : fail(LCSA_ERR_DEVICE, "device %d is not gfx950", dev);
+}
+
+lcsa_status check_view(const char* name, const lcsa_tensor* t, int64_t tokens, int heads,
+                       bool allow_null_data = false) {
+  if (!t) return fail(LCSA_ERR_NULL, "%s: tensor descriptor is NULL", name);
+  if (!t->data && !allow_null_data) return fail(LCSA_ERR_NULL, "%s: data is NULL", name);
+  if (t->dtype != LCSA_DTYPE_BF16) return fail(LCSA_ERR_INVALID, "%s: dtype must be bf16", name);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16)
+    return fail(LCSA_ERR_ALIGN, "%s: data pointer not 16-byte aligned", name);
+  if (t->stride_b < 0 || t->stride_s <= 0 || t->stride_h <= 0)
+    return fail(LCSA_ERR_INVALID, "%s: strides must be positive (batch stride >= 0)", name);
+  if (t->stride_b % 8 || t->stride_s % 8 || t->stride_h % 8)
+    return fail(LCSA_ERR_ALIGN, "%s: strides must be multiples of 8 elements", name);
+  (void)tokens;
+  (void)heads;
+  return LCSA_OK;
+}
+
+GridGeom make_geom(const lcsa_plan_s* p) {
+  const lcsa_plan_info& in = p->info;
+  GridGeom g;
+  g.heads = p->desc.heads;
+  g.grid_h = p->desc.grid_h;
+  g.grid_w = p->desc.grid_w;
+  g.block_h = in.block_h;
+  g.block_w = in.block_w;
+  g.log2_bw = 0;
+  while ((1 << g.log2_bw) < in.block_w) ++g.log2_bw;
+  g.nbh = in.nbh;
+  g.nbw = in.nbw;
+  g.nbf = in.blocks_per_frame;
+  g.nqb = in.nqb;
+  g.nkb = in.nkb;
+  g.q_frames = p->desc.q_frames;
+  g.kv_frames = in.kv_frames;
+  g.half = in.half_window;
+  g.k = in.k;
+  g.q_tokens = in.q_tokens;
+  return g;
+}
+
+View make_view(const lcsa_tensor* t) {
+  View v;
+  v.data = static_cast<const uint16_t*>(t->data);
+  v.sb = t->stride_b;
+  v.ss = t->stride_s;
+  v.sh = t->stride_h;
+  return v;
+}
+
+}  // namespace
+}  // namespace lcsa
+
+using lcsa::fail;
+
+extern "C" {
+
+lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                        int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                        void* d_workspace, size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_select: plan is NULL");
+  const lcsa_plan_info& in = plan->info;
+  lcsa_status st;
+  if ((st = lcsa::check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
+  if ((st = lcsa::check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
+  if (!d_row_ptr || !d_col_idx) return fail(LCSA_ERR_NULL, "lcsa_select: CSR buffers are NULL");
+  if (in.max_window > lcsa::kMaxWindow)
+    return fail(LCSA_ERR_SHAPE, "window of %d key blocks exceeds the select limit of %d",
+                in.max_window, lcsa::kMaxWindow);
+  if (!d_workspace || workspace_bytes < in.select_workspace_bytes)
+    return fail(LCSA_ERR_WORKSPACE, "select needs %llu workspace bytes, got %llu",
+                (unsigned long long)in.select_workspace_bytes,
+                (unsigned long long)workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256)
+    return fail(LCSA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((st = lcsa::check_device())) return st;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  lcsa::PoolKParams pk;
+  pk.g = lcsa::make_geom(plan);
+  pk.k = lcsa::make_view(k);
+  pk.kbar_t = static_cast<double*>(d_workspace);
+  hipError_t e = lcsa::launch_pool_k(pk, plan->desc.batch, in.block_tokens, s);
+  if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "pool_k launch: %s", hipGetErrorString(e));
+
+  lcsa::SelectParams sp;
+  sp.g = pk.g;
+  sp.q = lcsa::make_view(q);
+  sp.kbar_t = pk.kbar_t;
+  sp.row_ptr = d_row_ptr;
+  sp.col_idx = d_col_idx;
+  sp.scores = d_scores;
+  e = lcsa::launch_select(sp, plan->desc.batch, in.block_tokens, s);
+  if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "select launch: %s", hipGetErrorString(e));
+  return LCSA_OK;
+}
+
+lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                        const lcsa_tensor* v, const int32_t* d_row_ptr,
+                        const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
+                        float* d_lse, void* stream) {
+  lcsa::clear_error();
+  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_attend: plan is NULL");
+  const lcsa_plan_info& in = plan->info;
+  lcsa_status st;
+  if ((st = lcsa::check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
+  if ((st = lcsa::check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
+  if ((st = lcsa::check_view("v", v, in.kv_tokens, plan->desc.heads))) return st;
+  if ((st = lcsa::check_view("o", o, in.q_tokens, plan->desc.heads))) return st;
+  if (!d_row_ptr) return fail(LCSA_ERR_NULL, "lcsa_attend: row_ptr is NULL");
+  if (nnz < 0) return fail(LCSA_ERR_INVALID, "lcsa_attend: nnz %lld < 0", (long long)nnz);
+  if (nnz > 0 && !d_col_idx) return fail(LCSA_ERR_NULL, "lcsa_attend: col_idx is NULL");
+  if ((st = lcsa::check_device())) return st;
+
+  lcsa::AttendParams ap;
+  ap.g = lcsa::make_geom(plan);
+  ap.q = lcsa::make_view(q);
+  ap.k = lcsa::make_view(k);
+  ap.v = lcsa::make_view(v);
+  ap.o = static_cast<uint16_t*>(o->data);
+  ap.o_sb = o->stride_b;
+  ap.o_ss = o->stride_s;
+  ap.o_sh = o->stride_h;
+  ap.lse = d_lse;
+  ap.row_ptr = d_row_ptr;
+  ap.col_idx = d_col_idx;
+  ap.nnz = nnz;
+  ap.rows = in.rows;
+  ap.scale_log2 = static_cast<float>(in.scale * 1.4426950408889634);
+  const hipError_t e = lcsa::launch_attend(ap, in.block_tokens, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "attend launch: %s", hipGetErrorString(e));
+  return LCSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Kernel argument blocks of liblcsa (host and device).
+#pragma once
+
+#include <cstdint>
+
+namespace lcsa {
+
+// Geometry of the token grid and its blocks, shared by every kernel.
+struct GridGeom {
+  int32_t heads;
+  int32_t grid_h, grid_w;
+  int32_t block_h, block_w, log2_bw;  // block_w is a power of two
+  int32_t nbh, nbw, nbf;              // block rows / columns / blocks per frame
+  int32_t nqb, nkb;                   // query / key blocks
+  int32_t q_frames, kv_frames;
+  int32_t half;                       // window half-width in blocks
+  int32_t k;                          // kept-block budget
+  int64_t q_tokens;
+};
+
+struct View {
+  const uint16_t* data;  // bf16 bits
+  int64_t sb, ss, sh;    // strides in elements
+};
+
+struct PoolKParams {
+  GridGeom g;
+  View k;
+  double* kbar_t;  // [B][H][128][NKB]
+};
+
+struct SelectParams {
+  GridGeom g;
+  View q;
+  const double* kbar_t;  // [B][H][128][NKB]
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  double* scores;        // optional [B][H][NQB][NKB]
+};
+
+struct AttendParams {
+  GridGeom g;
+  View q, k, v;
+  uint16_t* o;
+  int64_t o_sb, o_ss, o_sh;
+  float* lse;            // optional [B][H][q_tokens]
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t nnz;
+  int64_t rows;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+}  // namespace lcsa

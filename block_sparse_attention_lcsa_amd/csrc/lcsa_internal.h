@@ -1,0 +1,41 @@
+// Private declarations shared by the host plan and the HIP entry points of
+// liblcsa.  Not installed; the public interface is include/lcsa.h.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "lcsa.h"
+
+struct lcsa_plan_s {
+  lcsa_desc desc;
+  lcsa_plan_info info;
+  std::vector<int32_t> row_ptr;      // rows + 1
+  std::vector<int32_t> frame_count;  // per spatial block position: min(k, |window|)
+};
+
+namespace lcsa {
+
+// Largest window (eligible key blocks of one query block) the select kernel
+// holds in LDS.
+constexpr int kMaxWindow = 1024;
+// Query frames scored together by one select workgroup.
+constexpr int kSelectFrames = 6;
+constexpr int kHeadDim = 128;
+
+// Record a formatted error for lcsa_last_error() and return the status.
+lcsa_status fail(lcsa_status st, const char* fmt, ...);
+void clear_error();
+
+// Spatial window bounds of block position (by, bx): inclusive ranges.
+inline void window_bounds(const lcsa_plan_info& in, int by, int bx, int* y0, int* y1, int* x0,
+                          int* x1) {
+  const int r = in.half_window;
+  *y0 = by - r < 0 ? 0 : by - r;
+  *y1 = by + r > in.nbh - 1 ? in.nbh - 1 : by + r;
+  *x0 = bx - r < 0 ? 0 : bx - r;
+  *x1 = bx + r > in.nbw - 1 ? in.nbw - 1 : bx + r;
+}
+
+}  // namespace lcsa

@@ -1,0 +1,211 @@
+/*
+ * liblcsa -- locality-constrained sparse attention (LCSA) for AMD Instinct
+ * MI355X (gfx950): block selection and block-sparse attention over a latent
+ * video token grid.
+ *
+ * The method: every query block keeps the k key blocks whose mean-pooled key
+ * scores highest against its mean-pooled query, among the key blocks that lie
+ * in a spatial window around it (any KV frame), and then attends with softmax
+ * over the tokens of those blocks only.  Attention limited to spatially local
+ * patches is LCSA as described in the agentlens FlashVSR summary ("How it
+ * works", item 2); pooling, mask selection and the CSR form of the mask are the
+ * attention glue named on the FlashVSR Hopper PR page ("What Was Actually
+ * Slow", "Rebuild sparse attention for Hopper"); the controls topk_ratio,
+ * local_range and kv_ratio come from the FlashVSR Inference skill page
+ * ("Non-Negotiable Streaming Contract").
+ *
+ * Conventions shared by every entry point:
+ *  - Tokens are in raster order (t, y, x) -> (t * grid_h + y) * grid_w + x,
+ *    t counting latent frames.  Q covers the q_frames newest frames of the KV
+ *    window; K and V cover all kv_frames frames of the window, oldest first.
+ *  - Q, K, V, O are bf16 with logical shape [batch, tokens, heads, head_dim];
+ *    head_dim is contiguous, other dims follow caller strides (elements).
+ *  - Blocks are 1 frame x block_h x block_w tokens; block index
+ *    kb = t * blocks_per_frame + by * (grid_w / block_w) + bx.
+ *  - The CSR block mask has one row per (b, h, query block):
+ *    row r = (b * heads + h) * nqb + qb; row_ptr has rows + 1 int32 entries;
+ *    col_idx holds key-block indices, strictly ascending inside a row.
+ *  - The library allocates no device memory.  The caller owns every buffer
+ *    (inputs, outputs, CSR, workspace) and the stream.
+ *  - All validation happens on the host before anything is enqueued; on an
+ *    error nothing is enqueued and the status says why (lcsa_last_error() has
+ *    the detail).  There is no fallback path of any kind.  Launches are
+ *    asynchronous: device faults surface at the caller's next synchronisation.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef LCSA_H_
+#define LCSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCSA_ABI_VERSION 1
+
+typedef int32_t lcsa_status;
+#define LCSA_OK 0
+#define LCSA_ERR_NULL 1       /* a required pointer is NULL */
+#define LCSA_ERR_INVALID 2    /* a descriptor value is out of range */
+#define LCSA_ERR_SHAPE 3      /* grid not tileable / sizes beyond limits */
+#define LCSA_ERR_ALIGN 4      /* data or strides not 16-byte aligned */
+#define LCSA_ERR_WORKSPACE 5  /* workspace missing or too small */
+#define LCSA_ERR_DEVICE 6     /* no current HIP device, or it is not gfx950 */
+#define LCSA_ERR_LAUNCH 7     /* the HIP runtime rejected a launch */
+#define LCSA_ERR_INTERNAL 8   /* allocation failure or unexpected state */
+
+#define LCSA_DTYPE_BF16 1
+
+/* Shape and control of one LCSA layer call.
+ *  batch, heads       > 0.
+ *  head_dim           must be 128 (the DiT's head size; NxDI FlashVSR
+ *                     contrib page, "Model Information").
+ *  grid_h, grid_w     tokens per latent frame (output pixels / 16).
+ *  q_frames           latent frames of the current chunk (queries), > 0.
+ *  cached_frames      earlier latent frames held in the KV cache, >= 0.
+ *  kv_ratio           KV window length bound: kv_frames = min(cached_frames +
+ *                     q_frames, ceil(kv_ratio * q_frames)); <= 0 means no
+ *                     bound; a value in (0, 1) is invalid.
+ *  block_t/h/w        block shape in tokens; all zero = automatic (1x8x16 if
+ *                     it tiles the grid, else 1x16x8); block_t must be 0 or 1
+ *                     and block_h * block_w must be 64 or 128.
+ *  local_range        odd window width in blocks (>= 1); the window is every
+ *                     KV frame and block rows/columns within local_range / 2.
+ *  topk_ratio         budget k = round-half-up(topk_ratio * blocks per frame)
+ *                     (values within 1e-9 of an integer snap to it), >= 1.
+ *  topk               > 0 overrides topk_ratio with an explicit k.
+ *  scale              softmax scale; 0 means 1 / sqrt(head_dim). */
+typedef struct lcsa_desc {
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t grid_h;
+  int32_t grid_w;
+  int32_t q_frames;
+  int32_t cached_frames;
+  int32_t block_t;
+  int32_t block_h;
+  int32_t block_w;
+  int32_t local_range;
+  int32_t topk;
+  double topk_ratio;
+  float kv_ratio;
+  float scale;
+} lcsa_desc;
+
+/* A device tensor view of logical shape [batch, tokens, heads, head_dim].
+ * data must be 16-byte aligned and stride_b/stride_s/stride_h (in elements)
+ * multiples of 8, so that every (token, head) row is a 256-byte aligned-16
+ * contiguous vector.  dtype must be LCSA_DTYPE_BF16. */
+typedef struct lcsa_tensor {
+  void* data;
+  int32_t dtype;
+  int32_t reserved;
+  int64_t stride_b;
+  int64_t stride_s;
+  int64_t stride_h;
+} lcsa_tensor;
+
+/* Everything the plan derived from a descriptor. */
+typedef struct lcsa_plan_info {
+  int32_t kv_frames;
+  int32_t blocks_per_frame;
+  int32_t nbh;                 /* block rows per frame */
+  int32_t nbw;                 /* block columns per frame */
+  int32_t nqb;                 /* query blocks = q_frames * blocks_per_frame */
+  int32_t nkb;                 /* key blocks = kv_frames * blocks_per_frame */
+  int32_t k;                   /* budget before clamping to a row's window */
+  int32_t block_h;
+  int32_t block_w;
+  int32_t block_tokens;
+  int32_t half_window;         /* local_range / 2 */
+  int32_t max_row_nnz;         /* largest min(k, |window|) over rows */
+  int32_t min_window;          /* smallest window size over query blocks */
+  int32_t max_window;          /* largest window size over query blocks */
+  int64_t rows;                /* batch * heads * nqb */
+  int64_t nnz;                 /* total selected blocks (row_ptr[rows]) */
+  int64_t q_tokens;
+  int64_t kv_tokens;
+  uint64_t select_workspace_bytes;
+  double scale;                /* softmax scale actually used */
+  double useful_flops;         /* 4 * head_dim * block_tokens^2 * nnz */
+} lcsa_plan_info;
+
+typedef struct lcsa_plan_s* lcsa_plan_t;
+
+/* Validate a descriptor and precompute geometry, budget, window sizes and the
+ * CSR row pointer.  Host only: needs no GPU.  On success *out owns a new plan
+ * (release with lcsa_plan_destroy); it is immutable and may be shared across
+ * threads and streams.  Errors: NULL, INVALID, SHAPE, INTERNAL. */
+lcsa_status lcsa_plan_create(const lcsa_desc* desc, lcsa_plan_t* out);
+
+/* Release a plan; NULL is a no-op. */
+void lcsa_plan_destroy(lcsa_plan_t plan);
+
+/* Copy the plan's derived values into *info.  Errors: NULL. */
+lcsa_status lcsa_plan_get_info(lcsa_plan_t plan, lcsa_plan_info* info);
+
+/* Copy the plan's CSR row pointer (rows + 1 int32 values, row r holds
+ * min(k, |window(qb)|) blocks) into host memory.  capacity is the number of
+ * int32 the caller provided.  Errors: NULL, WORKSPACE (capacity too small). */
+lcsa_status lcsa_plan_row_ptr(lcsa_plan_t plan, int32_t* host_out, int64_t capacity);
+
+/* Copy the window (eligible key blocks, ascending) of query block qb into
+ * host memory; *count receives its size.  Errors: NULL, INVALID (qb out of
+ * range), WORKSPACE (capacity smaller than the window). */
+lcsa_status lcsa_plan_window(lcsa_plan_t plan, int32_t qb, int32_t* host_out,
+                             int32_t capacity, int32_t* count);
+
+/* Block selection: mean-pool K per key block and Q per query block
+ * (float64 sums of the bf16 values), score each query block against every
+ * key block of its window (float64 dot products), keep the k best
+ * (descending score, ties to the lower block index) and emit them ascending
+ * as the CSR block mask.
+ *  q, k            device views (shape [batch, q_tokens | kv_tokens, heads,
+ *                  128]), read only.
+ *  d_row_ptr       device int32[rows + 1], written (equal to the plan's).
+ *  d_col_idx       device int32[nnz], written.
+ *  d_scores        NULL, or device double[batch * heads * nqb * nkb] that
+ *                  receives every pooled score (-inf outside the window).
+ *  d_workspace     device buffer of at least select_workspace_bytes bytes,
+ *                  256-byte aligned; its contents are scratch.
+ *  stream          hipStream_t to enqueue on (NULL = default stream).
+ * Errors: NULL, ALIGN, SHAPE, WORKSPACE, DEVICE, LAUNCH. */
+lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                        int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                        void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention forward: for each CSR row (b, h, query block) and
+ * every token of every key block in the row, z = scale * q.k; online softmax
+ * over those tokens; O = sum softmax(z) v, rounded to bf16 (nearest even);
+ * LSE = max z + ln(sum exp(z - max z)) in float32.
+ *  q, k, v, o      device views; o is written, the others are read.
+ *  d_row_ptr       device int32[rows + 1]; d_col_idx device int32[nnz].
+ *                  Any CSR is accepted: row bounds are clamped to [0, nnz]
+ *                  and block indices outside [0, nkb) are skipped in the
+ *                  kernel, so malformed content cannot read out of bounds.
+ *                  A row with no valid block yields O = 0 and LSE = -inf.
+ *  nnz             number of int32 in d_col_idx.
+ *  d_lse           NULL, or device float[batch * heads * q_tokens].
+ * Errors: NULL, ALIGN, INVALID (nnz < 0), DEVICE, LAUNCH. */
+lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                        const lcsa_tensor* v, const int32_t* d_row_ptr,
+                        const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
+                        float* d_lse, void* stream);
+
+/* Static text for a status code. */
+const char* lcsa_status_string(lcsa_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* lcsa_last_error(void);
+
+/* LCSA_ABI_VERSION of the loaded library. */
+int32_t lcsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCSA_H_ */

@@ -32,6 +32,8 @@ from __future__ import annotations
 
 import hashlib
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -141,19 +143,27 @@ def generate(desc: dict, seed: int = 0) -> Inputs:
     wy = rng.uniform(0.0, math.pi / 16, size=(H, D))
     wx = rng.uniform(0.0, math.pi / 16, size=(H, D))
     phi = rng.uniform(0.0, 2 * math.pi, size=(H, D))
-    out = {}
-    for name, s, t0 in (("q", sq, kvf - qf), ("k", skv, 0), ("v", skv, 0)):
-        noise = rng.standard_normal(size=(B, s, H, D), dtype=np.float32)
-        bits = np.empty((B, s, H, D), dtype=np.uint16)
-        nfr = s // fs
-        for f in range(nfr):
-            fld = _field_frame(t0 + f, gh, gw, wt, wy, wx, phi).reshape(fs, H, D)
-            sl = slice(f * fs, (f + 1) * fs)
-            for b in range(B):
-                val = 0.5 * noise[b, sl].astype(np.float64) + fld
-                bits[b, sl] = f32_to_bf16_bits(val.astype(np.float32))
-        del noise
-        out[name] = bits
+    noise = {name: rng.standard_normal(size=(B, n, H, D), dtype=np.float32)
+             for name, n in (("q", sq), ("k", skv), ("v", skv))}
+    out = {name: np.empty(noise[name].shape, dtype=np.uint16) for name in noise}
+    q0 = kvf - qf                      # first query frame inside the KV window
+    rows_per_piece = max(1, (1 << 21) // (H * D))
+
+    def one_frame(t):
+        fld = _field_frame(t, gh, gw, wt, wy, wx, phi).reshape(fs, H, D)
+        targets = [("k", t), ("v", t)] + ([("q", t - q0)] if t >= q0 else [])
+        for r0 in range(0, fs, rows_per_piece):
+            r1 = min(fs, r0 + rows_per_piece)
+            for name, f in targets:
+                sl = slice(f * fs + r0, f * fs + r1)
+                for b in range(B):
+                    val = 0.5 * noise[name][b, sl].astype(np.float64) + fld[r0:r1]
+                    out[name][b, sl] = f32_to_bf16_bits(val.astype(np.float32))
+
+    workers = max(1, min(kvf, len(os.sched_getaffinity(0)), 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one_frame, range(kvf)))
+    del noise
     h = hashlib.sha256()
     for name in ("q", "k", "v"):
         h.update(out[name].tobytes())

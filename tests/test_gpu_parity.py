@@ -1,0 +1,227 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle on
+the same seeded inputs.
+
+Select: row_ptr bit-exact; pooled scores within 1e-12 of the row scale
+(both sides sum in float64); selected blocks identical except at near-ties
+(oracle k-th score gap <= 1e-4 relative), which are counted and reported.
+Attend: bf16 output within max |err| <= 1e-2 and cosine >= 0.9999 of the
+oracle run on the GPU's own mask; LSE within 2e-3.  Small grids are compared
+element by element in full; the page workloads at their full sizes are
+compared on sampled CSR rows that the oracle computes one by one."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import lcsa_inputs as li
+import oracle
+from gpu_util import (check_mask, compare_output, bf16_to_np, device_qkv, host_inputs,
+                      oracle_select, say, to_device_bf16)
+
+pytestmark = pytest.mark.gpu
+
+import block_sparse_attention_lcsa_amd as lcsa  # noqa: E402  (fails loudly if not built)
+
+SMALL = ["tiny", "tiny_window", "small_edges", "small_16x8"]
+FULL = ["first_768x1280", "stream_768x1280", "first_768x1408", "first_2048x3840"]
+LSE_TOL = 2e-3
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say(f"[gpu] start {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+    say(f"[gpu] done  {request.node.nodeid}")
+
+
+def _f32(bits):
+    return li.bf16_bits_to_f32(bits)
+
+
+@pytest.mark.parametrize("name", SMALL + FULL)
+def test_select_parity(name):
+    desc, q, k, _ = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    say(f"  select {name}: rows {plan.info['rows']} nnz {plan.info['nnz']} "
+        f"window {plan.info['min_window']}..{plan.info['max_window']} k {plan.info['k']}")
+    rp, ci, sc = lcsa.select(plan, q, k, return_scores=True)
+    rp2, ci2 = lcsa.select(plan, q, k)           # path without the score dump
+    torch.cuda.synchronize()
+    g, rp_ref, ci_ref, s_ref = oracle_select(name)
+    s_gpu = sc.cpu().numpy()
+    assert np.array_equal(np.isneginf(s_gpu), np.isneginf(s_ref))
+    fin = np.isfinite(s_ref)
+    scale = float(np.abs(s_ref[fin]).max())
+    err = float(np.abs(s_gpu[fin] - s_ref[fin]).max())
+    say(f"  score max|err| {err:.3e} (scale {scale:.3e})")
+    assert err <= 1e-12 * scale
+    mism, ties = check_mask(g, rp_ref, ci_ref, s_ref, rp.cpu().numpy(), ci.cpu().numpy())
+    say(f"  rows {len(rp_ref) - 1}: mask mismatches {len(mism)}, all near-ties ({len(ties)})")
+    assert torch.equal(rp, rp2) and torch.equal(ci, ci2)
+
+
+@pytest.mark.parametrize("name", SMALL + ["stream_768x1280"])
+def test_attend_parity_full(name):
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+    torch.cuda.synchronize()
+    _, inp = host_inputs(name)
+    g = oracle.geometry(desc)
+    o_ref, lse_ref = oracle.attend(g, _f32(inp.q), _f32(inp.k), _f32(inp.v),
+                                   rp.cpu().numpy().astype(np.int64),
+                                   ci.cpu().numpy().astype(np.int64))
+    compare_output(bf16_to_np(o), o_ref, name)
+    lerr = float(np.abs(lse.cpu().numpy() - lse_ref).max())
+    say(f"  LSE max|err| {lerr:.3e}")
+    assert lerr <= LSE_TOL
+
+
+def _sample_rows(rows, n, seed):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(rows, size=min(n, rows), replace=False).tolist())
+    pick.update([0, rows - 1])
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_attend_parity_sampled(name):
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+    torch.cuda.synchronize()
+    _, inp = host_inputs(name)
+    g = oracle.geometry(desc)
+    rows = _sample_rows(plan.info["rows"], 48, seed=zlib.crc32(name.encode()))
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci.cpu().numpy().astype(np.int64)
+    ref = oracle.attend_rows(g, _f32(inp.q), _f32(inp.k), _f32(inp.v), rp_h, ci_h, rows)
+    o_h = bf16_to_np(o)
+    lse_h = lse.cpu().numpy()
+    got, want, lerr = [], [], 0.0
+    for b, h, qtok, orow, lrow in ref:
+        got.append(o_h[b, qtok, h, :])
+        want.append(orow)
+        lerr = max(lerr, float(np.abs(lse_h[b, h, qtok] - lrow).max()))
+    compare_output(np.stack(got), np.stack(want), f"{name} ({len(rows)} sampled rows)")
+    say(f"  LSE max|err| {lerr:.3e}")
+    assert lerr <= LSE_TOL
+
+
+def test_attend_dense_special_case():
+    """k = all key blocks with a covering window: plain dense attention."""
+    desc = dict(li.CONFIGS["tiny"], topk=8)
+    inp = li.generate(desc, seed=3)
+    q, k, v = (to_device_bf16(x) for x in (inp.q, inp.k, inp.v))
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    assert plan.info["nnz"] == plan.info["rows"] * plan.info["nkb"]
+    o = lcsa.attend(plan, q, k, v, rp, ci)
+    torch.cuda.synchronize()
+    g = oracle.geometry(desc)
+    rp_h, ci_h, _ = oracle.select(g, _f32(inp.q), _f32(inp.k))
+    o_ref, _ = oracle.attend(g, _f32(inp.q), _f32(inp.k), _f32(inp.v), rp_h, ci_h)
+    compare_output(bf16_to_np(o), o_ref, "dense")
+
+
+def test_attend_caller_csr_edge_rows():
+    """Empty rows, out-of-range block indices, a row over every key block and
+    a final row end beyond nnz (clamped)."""
+    name = "tiny_window"
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    _, rp_o, ci_o, _ = oracle_select(name)
+    rows = plan.info["rows"]
+    lists = [ci_o[rp_o[r]:rp_o[r + 1]].tolist() for r in range(rows)]
+    lists[0] = []
+    lists[1] = [-1, g.nkb + 3, 5, 2 ** 30]
+    lists[2] = list(range(g.nkb))
+    lists[3] = [-7]
+    rp_h = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int64)
+    ci_h = np.asarray([c for x in lists for c in x], dtype=np.int64)
+    rp_dev_h = rp_h.copy()
+    rp_dev_h[-1] += 10                      # end past nnz: the kernel clamps
+    rp_d = torch.from_numpy(rp_dev_h.astype(np.int32)).cuda()
+    ci_d = torch.from_numpy(ci_h.astype(np.int32)).cuda()
+    o, lse = lcsa.attend(plan, q, k, v, rp_d, ci_d, return_lse=True)
+    torch.cuda.synchronize()
+    _, inp = host_inputs(name)
+    o_ref, lse_ref = oracle.attend(g, _f32(inp.q), _f32(inp.k), _f32(inp.v), rp_h, ci_h)
+    compare_output(bf16_to_np(o), o_ref, "edge rows")
+    lse_h = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lse_h), np.isneginf(lse_ref))
+    fin = np.isfinite(lse_ref)
+    assert float(np.abs(lse_h[fin] - lse_ref[fin]).max()) <= LSE_TOL
+    q_empty = oracle.block_tokens(g, 0)
+    assert np.all(bf16_to_np(o)[0, q_empty, 0, :] == 0)
+
+
+def test_strided_views_and_kv_cache_window():
+    """Q/K/V as slices of a packed QKV tensor, O written into a strided view,
+    and K/V of a streaming call as a window of a longer cache: bitwise equal
+    to the contiguous call."""
+    name = "small_16x8"
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    o_ref = lcsa.attend(plan, q, k, v, rp, ci)
+    B, S, H, D = q.shape
+    qkv = torch.empty((B, S, 3, H, D), dtype=torch.bfloat16, device="cuda")
+    qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2] = q, k, v
+    obuf = torch.zeros((B, S, H, 2 * D), dtype=torch.bfloat16, device="cuda")
+    out = obuf[..., D:]
+    rp2, ci2 = lcsa.select(plan, qkv[:, :, 0], qkv[:, :, 1])
+    lcsa.attend(plan, qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], rp2, ci2, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp2) and torch.equal(ci, ci2)
+    assert torch.equal(out, o_ref) and torch.all(obuf[..., :D] == 0)
+
+    name = "small_edges"       # 2 query frames, KV window of 3 frames
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    o_ref = lcsa.attend(plan, q, k, v, rp, ci)
+    fs = desc["grid_h"] * desc["grid_w"]
+    cache_k = torch.zeros((B, k.shape[1] + 2 * fs, k.shape[2], D), dtype=torch.bfloat16, device="cuda")
+    cache_v = torch.zeros_like(cache_k)
+    cache_k[:, 2 * fs:], cache_v[:, 2 * fs:] = k, v
+    kw, vw = cache_k[:, 2 * fs:], cache_v[:, 2 * fs:]
+    rp2, ci2 = lcsa.select(plan, q, kw)
+    o2 = lcsa.attend(plan, q, kw, vw, rp2, ci2)
+    torch.cuda.synchronize()
+    assert torch.equal(ci, ci2) and torch.equal(o_ref, o2)
+
+
+def test_batch_two():
+    name = "small_edges"
+    desc, q, k, v = device_qkv(name, batch=2)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci, sc = lcsa.select(plan, q, k, return_scores=True)
+    o = lcsa.attend(plan, q, k, v, rp, ci)
+    torch.cuda.synchronize()
+    g, rp_ref, ci_ref, s_ref = oracle_select(name, batch=2)
+    check_mask(g, rp_ref, ci_ref, s_ref, rp.cpu().numpy(), ci.cpu().numpy())
+    _, inp = host_inputs(name, batch=2)
+    o_ref, _ = oracle.attend(g, _f32(inp.q), _f32(inp.k), _f32(inp.v), rp_ref, ci_ref)
+    compare_output(bf16_to_np(o), o_ref, "batch 2")
+
+
+def test_deterministic_repeat():
+    name = "first_768x1280"
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    outs = []
+    for _ in range(2):
+        rp, ci = lcsa.select(plan, q, k)
+        o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+        outs.append((rp, ci, o, lse))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)

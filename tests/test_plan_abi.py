@@ -1,0 +1,173 @@
+"""Host-side tests of liblcsa through its C ABI: the library loads and exports
+every symbol include/lcsa.h declares, the plan reproduces the oracle's
+geometry, budget, windows and CSR row pointer, and each error status is
+reachable from the host.  No kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import lcsa_inputs as li
+import oracle
+
+lcsa = pytest.importorskip("block_sparse_attention_lcsa_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcsa.h")
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcsa_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_what_binding_lists():
+    assert _declared_functions() == sorted(lcsa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lcsa.lib_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lcsa.lib_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared_functions():
+        assert name in exported, name
+
+
+def test_abi_version_and_status_strings():
+    assert lcsa.abi_version() == 1
+    lib = ctypes.CDLL(lcsa.lib_path())
+    lib.lcsa_status_string.restype = ctypes.c_char_p
+    texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
+    assert len(texts) == 9
+    assert lib.lcsa_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("name", list(li.CONFIGS))
+def test_plan_matches_oracle_geometry(name):
+    desc = li.CONFIGS[name]
+    g = oracle.geometry(desc)
+    p = lcsa.Plan.from_desc(desc)
+    inf = p.info
+    assert inf["kv_frames"] == g.kv_frames
+    assert (inf["nbh"], inf["nbw"], inf["blocks_per_frame"]) == (g.nbh, g.nbw, g.nbf)
+    assert (inf["nqb"], inf["nkb"]) == (g.nqb, g.nkb)
+    assert (inf["block_h"], inf["block_w"], inf["block_tokens"]) == (g.block_h, g.block_w, g.block_tokens)
+    assert inf["k"] == min(g.k, g.nkb)
+    assert inf["half_window"] == g.half
+    assert inf["q_tokens"] == g.q_tokens and inf["kv_tokens"] == g.kv_tokens
+    assert abs(inf["scale"] - g.scale) < 1e-15
+    sizes = [len(oracle.window(g, qb)) for qb in range(g.nqb)]
+    assert (inf["min_window"], inf["max_window"]) == (min(sizes), max(sizes))
+    counts = [min(g.k, n) for n in sizes]
+    assert inf["max_row_nnz"] == max(counts)
+    rp = np.concatenate([[0], np.cumsum(counts * (g.batch * g.heads))])
+    assert inf["rows"] == len(rp) - 1 and inf["nnz"] == rp[-1]
+    assert np.array_equal(p.row_ptr(), rp)
+    assert inf["useful_flops"] == oracle.useful_flops(g, rp)
+    for qb in range(0, g.nqb, max(1, g.nqb // 37)):
+        assert np.array_equal(p.window(qb), oracle.window(g, qb))
+
+
+def _desc(**over):
+    d = dict(li.CONFIGS["first_768x1280"])
+    d.update(over)
+    return d
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), "LCSA_ERR_INVALID"),
+    (dict(heads=0), "LCSA_ERR_INVALID"),
+    (dict(q_frames=0), "LCSA_ERR_INVALID"),
+    (dict(cached_frames=-1), "LCSA_ERR_INVALID"),
+    (dict(local_range=10), "LCSA_ERR_INVALID"),
+    (dict(local_range=0), "LCSA_ERR_INVALID"),
+    (dict(kv_ratio=0.5), "LCSA_ERR_INVALID"),
+    (dict(topk_ratio=0.0, topk=0), "LCSA_ERR_INVALID"),
+    (dict(topk=-2), "LCSA_ERR_INVALID"),
+    (dict(scale=-1.0), "LCSA_ERR_INVALID"),
+    (dict(block_t=2), "LCSA_ERR_INVALID"),
+    (dict(block_h=8, block_w=0), "LCSA_ERR_INVALID"),
+    (dict(grid_h=44, grid_w=44), "LCSA_ERR_SHAPE"),
+    (dict(block_t=1, block_h=4, block_w=4), "LCSA_ERR_SHAPE"),
+    (dict(block_t=1, block_h=8, block_w=32), "LCSA_ERR_SHAPE"),
+    (dict(grid_h=48, grid_w=72, block_t=1, block_h=8, block_w=16), "LCSA_ERR_SHAPE"),
+])
+def test_plan_rejects(over, status):
+    with pytest.raises(lcsa.LcsaError) as ei:
+        lcsa.Plan.from_desc(_desc(**over))
+    assert ei.value.name == status
+    assert str(ei.value).count(":") >= 2   # carries the detail message
+
+
+def test_plan_auto_block_16x8_and_null_args():
+    p = lcsa.Plan.from_desc(_desc(grid_w=88))
+    assert (p.info["block_h"], p.info["block_w"]) == (16, 8)
+    lib = ctypes.CDLL(lcsa.lib_path())
+    lib.lcsa_plan_create.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.lcsa_plan_create(None, None) == 1
+    lib.lcsa_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.lcsa_plan_destroy(None)   # no-op
+
+
+def test_row_ptr_capacity_and_window_range():
+    p = lcsa.Plan.from_desc(li.CONFIGS["tiny"])
+    lib = ctypes.CDLL(lcsa.lib_path())
+    lib.lcsa_plan_row_ptr.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    buf = np.zeros(4, dtype=np.int32)
+    assert lib.lcsa_plan_row_ptr(p.handle, buf.ctypes.data, 4) == 5   # WORKSPACE
+    with pytest.raises(lcsa.LcsaError) as ei:
+        p.window(p.info["nqb"])
+    assert ei.value.name == "LCSA_ERR_INVALID"
+
+
+def _fake_view(addr=0x10000, sb=0, ss=256, sh=128):
+    return lcsa.LcsaTensor(data=addr, dtype=1, reserved=0, stride_b=sb, stride_s=ss, stride_h=sh)
+
+
+def _select(p, q, k, rp=0x20000, ci=0x30000, ws=0x40000, ws_bytes=None):
+    lib = lcsa._lib
+    wsb = p.info["select_workspace_bytes"] if ws_bytes is None else ws_bytes
+    return lib.lcsa_select(p.handle, ctypes.byref(q), ctypes.byref(k), rp, ci, None, ws, wsb, None)
+
+
+def _attend(p, q, k, v, o, nnz=8):
+    lib = lcsa._lib
+    return lib.lcsa_attend(p.handle, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                           0x20000, 0x30000, nnz, ctypes.byref(o), None, None)
+
+
+def test_entry_point_validation_statuses():
+    """Argument checks run on the host before any HIP call; the fake device
+    addresses are never dereferenced because every call here fails first."""
+    p = lcsa.Plan.from_desc(li.CONFIGS["tiny"])
+    good = _fake_view()
+    assert _select(p, _fake_view(addr=0x10008), good) == 4            # ALIGN data
+    assert _select(p, _fake_view(ss=250), good) == 4                  # ALIGN stride
+    assert _select(p, _fake_view(addr=0), good) == 1                  # NULL data
+    assert _select(p, good, good, rp=0) == 1                          # NULL CSR
+    assert _select(p, good, good, ws_bytes=16) == 5                   # WORKSPACE
+    assert _select(p, good, good, ws=0x40010) == 4                    # ALIGN workspace
+    bad_dtype = _fake_view(); bad_dtype.dtype = 7
+    assert _select(p, bad_dtype, good) == 2                           # INVALID dtype
+    assert _attend(p, good, good, good, good, nnz=-1) == 2            # INVALID nnz
+    assert _attend(p, good, good, _fake_view(addr=0x10004), good) == 4
+    assert lcsa._lib.lcsa_select(None, None, None, None, None, None, None, 0, None) == 1
+    big = lcsa.Plan.from_desc(dict(li.CONFIGS["first_2048x3840"], local_range=15))
+    assert big.info["max_window"] > 1024
+    assert _select(big, good, good) == 3                              # SHAPE: window limit
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device status on CPU hosts")
+def test_no_device_status_on_cpu_host():
+    p = lcsa.Plan.from_desc(li.CONFIGS["tiny"])
+    good = _fake_view()
+    assert _select(p, good, good) == 6                                # DEVICE
+    assert _attend(p, good, good, good, good) == 6
