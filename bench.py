@@ -1,0 +1,228 @@
+"""Benchmark of one LCSA layer call (select + attend) on one MI355X.
+
+A step is one pass of the whole hot path on one chunk: host plan, pooled
+block scores + top-k CSR mask (lcsa_select), block-sparse attention
+(lcsa_attend).  Default workload: the first chunk at 768x1280 output
+(6 latent frames x 48x80 tokens = 23040 tokens, 12 heads x 128, 128-token
+blocks, local_range 11, sparse_ratio 2.0 -> 60 kept blocks per query block),
+seeded synthetic bf16 inputs resident in HBM before timing starts.
+
+Prints ONE JSON line.  value = useful attention TFLOP/s of the whole step
+(useful FLOP = 4 * 128 * 128 * 128 per selected block pair; skipped blocks do
+not count), ms_per_step = select+attend ms per chunk.  roofline = the attend
+kernel (MFMA-bound) timed with HIP events on its stream; cpu_baseline = the
+float64 CPU oracle on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calibration   # plain copy of known size (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+ATTEND_SRC = os.path.join(ROOT, "block_sparse_attention_lcsa_amd", "csrc", "attend.hip")
+
+
+def _src_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def _traffic(workload):
+    """HBM bytes per attend launch from the committed rocprofv3 counter runs,
+    if they were taken on the current attend kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("attend_src_sha256") != _src_sha(ATTEND_SRC):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(name, desc, inp, useful_flops):
+    """Time the oracle as it stands on a bounded sample and scale to a step."""
+    import numpy as np
+    import lcsa_inputs as li
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    g = oracle.geometry(desc)
+    qf, kf, vf = (li.bf16_bits_to_f32(x) for x in (inp.q, inp.k, inp.v))
+    t0 = time.perf_counter()
+    rp, ci, _ = oracle.select(g, qf, kf)
+    t_sel = time.perf_counter() - t0
+    rows = len(rp) - 1
+    # rows sampled evenly; grow the sample until ~10 s of attention work
+    n = max(8, rows // 64)
+    t_att, done = 0.0, 0
+    while True:
+        sample = np.linspace(0, rows - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attend_rows(g, qf, kf, vf, rp, ci, sample)
+        t_att = time.perf_counter() - t0
+        done = n
+        if t_att >= 8.0 or n >= rows:
+            break
+        n = min(rows, int(n * max(2.0, 10.0 / max(t_att, 1e-3))))
+    step_s = t_sel + t_att * rows / done
+    return {
+        "value": useful_flops / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "ms_per_step": step_s * 1e3,
+        "sample": (f"{name}: oracle select on all {rows} CSR rows ({t_sel:.2f} s) + oracle "
+                   f"attention on {done} of {rows} rows ({t_att:.2f} s), scaled to the full "
+                   f"step; float64 numpy, {blas_threads} BLAS threads, "
+                   f"{len(os.sched_getaffinity(0))} host cores visible"),
+    }
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="first_768x1280")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the LCSA path runs per (batch, head) with no "
+              "cross-GPU exchange, and this build has no multi-GPU path. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+    import block_sparse_attention_lcsa_amd as lcsa
+    import lcsa_inputs as li
+
+    name = args.workload
+    desc = dict(li.CONFIGS[name])
+    inp = li.generate(desc, seed=args.seed)
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    plan = lcsa.Plan.from_desc(desc)
+    info = plan.info
+    flops = float(info["useful_flops"])
+    ws = torch.empty(max(int(info["select_workspace_bytes"]), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        p = lcsa.Plan.from_desc(desc)                      # host plan (per shape)
+        if ev:
+            ev[0].record(stream)
+        rp, ci = lcsa.select(p, q, k, workspace=ws)
+        if ev:
+            ev[1].record(stream)
+        lcsa.attend(p, q, k, v, rp, ci, out=out)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+
+    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    att_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    gpu_ms = t_start.elapsed_time(t_end) / args.steps
+    att_avg = float(np.mean(att_ms))
+    sel_avg = float(np.mean(sel_ms))
+    step_ms = max(wall_ms, gpu_ms)
+    achieved = flops / (att_avg * 1e-3) / 1e12
+
+    res = {
+        "metric": "LCSA attend useful TFLOP/s + fraction of bf16 MFMA peak; select+attend ms/chunk",
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "batch": desc["batch"], "heads": desc["heads"], "head_dim": desc["head_dim"],
+            "q_tokens": info["q_tokens"], "kv_tokens": info["kv_tokens"],
+            "block": [info["block_h"], info["block_w"]], "local_range": desc["local_range"],
+            "k": info["k"], "selected_pairs": info["nnz"], "useful_tflop": flops / 1e12,
+            "seed": args.seed, "inputs_sha256": inp.sha256,
+        },
+        "select_ms": sel_avg,
+        "attend_ms": att_avg,
+        "select_ms_p10_p90": [float(np.percentile(sel_ms, 10)), float(np.percentile(sel_ms, 90))],
+        "attend_ms_p10_p90": [float(np.percentile(att_ms, 10)), float(np.percentile(att_ms, 90))],
+        "attend_tflops": achieved,
+        "attend_frac_of_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": _traffic(name),
+        },
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(name, desc, inp, flops)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,19 +9,29 @@
 // reading Q/K/V through strides in raster token order ("strided IO",
 // "zero-copy raster V handling") and a CSR block list per query block.
 //
-// Layout of the work (wave64, 32x32x16 bf16 MFMA):
-//  * Each wave owns 32 query rows.  It computes S^T = K Q^T so that every lane
+// Work layout (wave64, 32x32x16 bf16 MFMA, BT = tokens per block):
+//  * Each wave owns 32 query rows and computes S^T = K Q^T, so every lane
 //    holds the scores of ONE query (lane & 31) against 16 keys per 32-key
-//    tile; row max and row sum are per-lane plus one exchange with lane ^ 32.
-//  * K rows feed MFMA operand A in a permuted order pi(m) chosen so that the
-//    S^T accumulator register r of lane half g holds key 16g + r.  Those 8-key
-//    runs are exactly MFMA operand B of O^T = V^T P^T, so P never leaves the
-//    registers.  The O^T accumulator is again one query per lane, so the
+//    tile: row max / row sum are per lane plus one permlane32 swap.
+//  * K rows feed MFMA operand A in a permuted order chosen so that S^T
+//    accumulator register r of lane half g holds key 16g + r.  Those 8-key
+//    runs are exactly MFMA operand B of O^T = V^T P^T: P never leaves the
+//    registers, and the O^T accumulator is again one query per lane, so the
 //    online-softmax rescale is a per-lane scalar.
-//  * K is staged row-major and V transposed (V^T: [d][key]) in LDS, both with
-//    an XOR swizzle on 16-byte chunks so the MFMA operand reads and the tile
-//    writes spread over the banks.  The next block's K/V are loaded from HBM
-//    into registers while the current block is computed.
+//  * K and V tiles stream HBM -> LDS with direct-to-LDS 16-byte loads (no
+//    register staging), both row-major [key][128] with a 16-byte-chunk XOR
+//    swizzle.  Operand A of V^T P^T is read with the LDS transpose read
+//    (ds_read_b64_tr_b16), which returns 4 keys of one channel per lane.
+//  * K and V buffers have separate lifetimes: V(i) streams in while S(i) and
+//    the softmax run, K(i+1) while the softmax and PV(i) run.  Barriers are
+//    raw s_barrier with explicit vmcnt waits, so in-flight tile loads are
+//    not drained at every barrier.
+//  * Lazy rescale: the running max only moves when some lane's block max
+//    exceeds it by more than 2^8; exp2 arguments stay <= 8, and O and the row
+//    sum share the same stale reference, so the result is unchanged.
+//  * Rows are laid out so each XCD (workgroup id mod 8) walks a contiguous
+//    range of rows (same head, neighbouring query blocks), which share most
+//    of their selected key blocks in that XCD's L2.
 
 #include <hip/hip_runtime.h>
 
@@ -32,31 +42,28 @@ namespace lcsa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+constexpr float kLazyRescale = 8.0f;   // log2 units
+constexpr int kXcds = 8;
 
 __device__ inline uint4 load16(const uint16_t* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
-
 __device__ inline bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Chunk swizzles (16-byte chunks).  K tile: row j (key), 16 chunks of 8
-// channels.  V^T tile: row d (channel), BT/8 chunks of 8 keys.
+// 16-byte chunk swizzles of the row-major [key][128] tiles (16 chunks per
+// 256-byte row).  K: conflict-free ds_read_b128 for the permuted key rows of
+// an S^T operand.  V: conflict-free transpose reads (4 rows x 4 chunks per
+// half wave).
 __device__ inline int swz_k(int j) { return (j & 7) | (((j >> 4) & 1) << 3); }
-__device__ inline int swz_v(int d) { return (d & 15) ^ ((d >> 4) & 7); }
+__device__ inline int swz_v(int j) { return (j & 3) << 2; }
 
-// A-operand row m of a 32-key S^T tile reads key pi(m): with the 32x32 MFMA
-// accumulator layout (row 8*(r/4) + 4*g + r%4 in register r of lane half g)
-// this puts key 16*g + r into register r.
+// A-operand row m of a 32-key S^T tile reads key key_perm(m): with the 32x32
+// MFMA accumulator layout (row 8*(r/4) + 4*g + r%4 in register r of lane
+// half g) this puts key 16*g + r into register r.
 __device__ inline int key_perm(int m) { return (((m >> 2) & 1) << 4) | ((m >> 3) << 2) | (m & 3); }
-
-// 16-bit lane `sel` of word pair (lo word a, hi word b).
-__device__ inline uint32_t pick_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ inline uint32_t pick_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-__device__ inline uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
 
 __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, int j) {
   const int y = by * g.block_h + (j >> g.log2_bw);
@@ -64,30 +71,82 @@ __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, 
   return ((int64_t)t * g.grid_h + y) * g.grid_w + x;
 }
 
+// Workgroup barrier that completes this wave's own LDS reads (lgkmcnt) but
+// leaves its in-flight HBM -> LDS tile loads (vmcnt) running.
+__device__ inline void barrier_raw() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane direct load HBM -> LDS: lane L's 16 bytes from
+// sbase + voff land at LDS address lds_addr + 16 * L.  Issued as inline asm
+// so that the compiler's conservative LDS-DMA tracking (which would drain all
+// in-flight tile loads before any LDS read) does not apply; ordering is
+// enforced with wait_vmcnt and barrier_raw instead.  The instruction writes
+// only LDS and has no register result.
+__device__ inline void dma16(const void* sbase, int voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int BT>
 struct Tile {
   static constexpr int kWaves = BT / 32;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKeyTiles = BT / 32;
-  static constexpr int kVChunks = BT / 8;        // 16-byte chunks per V^T row
-  static constexpr int kKBytes = BT * 256;       // K tile: BT x 128 bf16
-  static constexpr int kVBytes = 128 * BT * 2;   // V^T tile: 128 x BT bf16
-  static constexpr int kRowStep = BT / 8;        // K rows between a thread's loads
+  static constexpr int kTileBytes = BT * 256;               // BT x 128 bf16
+  static constexpr int kLoads = kTileBytes / (kThreads * 16); // 16-byte loads per lane per tile
 };
 
 template <int BT>
-__global__ void __launch_bounds__(BT * 2) attend_fwd_kernel(AttendParams p) {
+__global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   using T = Tile<BT>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::kKBytes + T::kVBytes];
-  unsigned char* const ks = smem;
-  unsigned char* const vt = smem + T::kKBytes;
+  static_assert(T::kLoads == 8, "8 direct loads per lane per tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds[T::kTileBytes];
 
   const GridGeom& g = p.g;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  const int64_t row = blockIdx.x;
+  // XCD-aware row order: workgroup ids go round-robin over the XCDs; give
+  // XCD x the contiguous row range [start_x, start_x + count_x).
+  int64_t row;
+  {
+    const int64_t pid = blockIdx.x, n = p.rows;
+    const int64_t xcd = pid % kXcds, idx = pid / kXcds;
+    const int64_t per = n / kXcds, rem = n % kXcds;
+    row = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  }
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;
   const int h = (int)(bh % g.heads);
@@ -95,7 +154,7 @@ __global__ void __launch_bounds__(BT * 2) attend_fwd_kernel(AttendParams p) {
   const int tq = qb / g.nbf, qpos = qb - tq * g.nbf;
   const int qby = qpos / g.nbw, qbx = qpos - qby * g.nbw;
 
-  // Q fragments: this lane's query row, channels 16s + 8*half .. +7.
+  // Q fragments (MFMA operand B of S^T): query lane&31, channels 16s+8*half..+7.
   const int qi = wave * 32 + l32;
   const int64_t qtok = block_token(g, tq, qby, qbx, qi);
   bf16x8_t qf[8];
@@ -105,39 +164,78 @@ __global__ void __launch_bounds__(BT * 2) attend_fwd_kernel(AttendParams p) {
     for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(load16(qrow + 16 * s + 8 * half));
   }
 
-  int64_t start = p.row_ptr[row], end = p.row_ptr[row + 1];
-  start = start < 0 ? 0 : (start > p.nnz ? p.nnz : start);
-  end = end < start ? start : (end > p.nnz ? p.nnz : end);
+  // The CSR is read-only here: read it through the constant address space so
+  // the (uniform) reads become scalar loads, which do not wait on the vector
+  // memory counter that tracks the in-flight tile loads.
+  const __attribute__((address_space(4))) int32_t* row_ptr =
+      (const __attribute__((address_space(4))) int32_t*)p.row_ptr;
+  const __attribute__((address_space(4))) int32_t* col_idx =
+      (const __attribute__((address_space(4))) int32_t*)p.col_idx;
+  // Row bounds clamped to [0, nnz] (nnz < 2^31 is checked on the host).
+  const int nnz = (int)p.nnz;
+  int start = row_ptr[row], end = row_ptr[row + 1];
+  start = start < 0 ? 0 : (start > nnz ? nnz : start);
+  end = end < start ? start : (end > nnz ? nnz : end);
+  start = __builtin_amdgcn_readfirstlane(start);
+  end = __builtin_amdgcn_readfirstlane(end);
 
-  const uint16_t* kbase = p.k.data + (int64_t)b * p.k.sb + (int64_t)h * p.k.sh;
-  const uint16_t* vbase = p.v.data + (int64_t)b * p.v.sb + (int64_t)h * p.v.sh;
-  const int c = tid & 15;            // channel chunk this thread loads
-  const int jk0 = tid >> 4;          // first K row this thread loads
-  const int jv0 = (tid >> 4) * 8;    // first of the 8 V rows this thread loads
-
-  uint4 kr[8], vr[8];
-  auto load_block = [&](int kb) {
+  // Per-lane byte offsets (inside one key block) of the 8 direct loads of a
+  // tile: load i of wave w fills LDS slots [(i*waves + w)*64, +64); slot s
+  // holds row s>>4, logical chunk (s&15) ^ swizzle(row).
+  const int row_stride_k = (int)(p.k.ss * 2), row_stride_v = (int)(p.v.ss * 2);
+  int koff[8], voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = (i * T::kWaves + wave) * 64 + lane;
+    const int j = s >> 4;
+    const int tj = (j >> g.log2_bw) * g.grid_w + (j & (g.block_w - 1));  // token offset in block
+    koff[i] = tj * row_stride_k + (((s & 15) ^ swz_k(j)) << 4);
+    voff[i] = tj * row_stride_v + (((s & 15) ^ swz_v(j)) << 4);
+  }
+  const char* kbase = reinterpret_cast<const char*>(p.k.data + (int64_t)b * p.k.sb + (int64_t)h * p.k.sh);
+  const char* vbase = reinterpret_cast<const char*>(p.v.data + (int64_t)b * p.v.sb + (int64_t)h * p.v.sh);
+  auto block_offset = [&](int kb, int64_t ss2) {
     const int t = kb / g.nbf, ps = kb - t * g.nbf;
     const int kby = ps / g.nbw, kbx = ps - kby * g.nbw;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t tk = block_token(g, t, kby, kbx, jk0 + T::kRowStep * i);
-      kr[i] = load16(kbase + tk * p.k.ss + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t tv = block_token(g, t, kby, kbx, jv0 + i);
-      vr[i] = load16(vbase + tv * p.v.ss + c * 8);
-    }
+    const int64_t tok0 = ((int64_t)t * g.grid_h + (int64_t)kby * g.block_h) * g.grid_w + (int64_t)kbx * g.block_w;
+    return tok0 * ss2;
   };
-  auto next_valid = [&](int64_t i) {
+  const uint32_t k_lds_addr = lds_address(k_lds) + wave * 1024;
+  const uint32_t v_lds_addr = lds_address(v_lds) + wave * 1024;
+  auto issue_k = [&](int kb) {
+    const char* src = kbase + block_offset(kb, row_stride_k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(src, koff[i], k_lds_addr + i * T::kWaves * 1024);
+  };
+  auto issue_v = [&](int kb) {
+    const char* src = vbase + block_offset(kb, row_stride_v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(src, voff[i], v_lds_addr + i * T::kWaves * 1024);
+  };
+  // Next CSR position >= i holding a valid key block (uniform; scalar loads).
+  auto next_valid = [&](int i) {
+    i = __builtin_amdgcn_readfirstlane(i);
     while (i < end) {
-      const int kb = __builtin_amdgcn_readfirstlane(p.col_idx[i]);
+      const int kb = col_idx[i];
       if (kb >= 0 && kb < g.nkb) break;
-      ++i;
+      i = __builtin_amdgcn_readfirstlane(i + 1);
     }
     return i;
   };
+
+  // LDS read addresses of this lane.
+  // S^T operand A: row 32*kt + key_perm(l32), chunk (2*st + half) ^ swz_k.
+  const int kp = key_perm(l32);
+  const int ksw = swz_k(kp);
+  const unsigned char* krow = k_lds + kp * 256;
+  // V^T operand A via transpose reads: 16-lane group G = lane >> 4 covers
+  // channels 32*dt + 16*(G&1) .. +15 and keys 32*kt + 16*half + 8*s2 + 4*r
+  // + 0..3; lane s of the group points at row (s >> 2) of that 4-key run,
+  // channels 4*(s & 3) .. +3 of the group's 16.
+  const int gs = lane & 15, grp = lane >> 4;
+  const unsigned char* vrow = v_lds + (16 * half + (gs >> 2)) * 256 + (gs & 1) * 8;
+  const int vchunk_lo = 2 * (grp & 1) + ((gs & 3) >> 1);
+  const int vsw = swz_v(gs >> 2);
 
   f32x16_t o[4];
 #pragma unroll
@@ -147,66 +245,52 @@ __global__ void __launch_bounds__(BT * 2) attend_fwd_kernel(AttendParams p) {
   float m_run = -__builtin_huge_valf(), l_run = 0.0f;
   const float sl2 = p.scale_log2;
 
-  int64_t it = next_valid(start);
-  if (it < end) load_block(__builtin_amdgcn_readfirstlane(p.col_idx[it]));
+  int it = next_valid(start);
+  if (it < end) issue_k(col_idx[it]);
 
   while (it < end) {
-    __syncthreads();  // every wave is done with the previous tiles
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = jk0 + T::kRowStep * i;
-      *reinterpret_cast<uint4*>(ks + j * 256 + ((c ^ swz_k(j)) & 15) * 16) = kr[i];
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int wi = dd >> 1;
-      uint4 w;
-      if (dd & 1) {
-        w.x = pick_hi(word(vr[0], wi), word(vr[1], wi));
-        w.y = pick_hi(word(vr[2], wi), word(vr[3], wi));
-        w.z = pick_hi(word(vr[4], wi), word(vr[5], wi));
-        w.w = pick_hi(word(vr[6], wi), word(vr[7], wi));
-      } else {
-        w.x = pick_lo(word(vr[0], wi), word(vr[1], wi));
-        w.y = pick_lo(word(vr[2], wi), word(vr[3], wi));
-        w.z = pick_lo(word(vr[4], wi), word(vr[5], wi));
-        w.w = pick_lo(word(vr[6], wi), word(vr[7], wi));
-      }
-      const int d = 8 * c + dd;
-      const int x = tid >> 4;
-      *reinterpret_cast<uint4*>(vt + d * (BT * 2) + ((x ^ swz_v(d)) & (T::kVChunks - 1)) * 16) = w;
-    }
-    __syncthreads();  // tiles visible
+    const int kb = col_idx[it];
+    wait_vmcnt<0>();          // K(it) landed (this wave's share)
+    barrier_raw();            // ... everyone's; V buffer free (PV of it-1 done)
+    issue_v(kb);
 
-    const int64_t nx = next_valid(it + 1);
-    if (nx < end) load_block(__builtin_amdgcn_readfirstlane(p.col_idx[nx]));
-
-    // ---- S^T = K Q^T, one 32x32 tile per 32 keys
+    // ---- S^T = K Q^T
     f32x16_t s[T::kKeyTiles];
 #pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt) {
+    for (int kt = 0; kt < T::kKeyTiles; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
-      const int j = 32 * kt + key_perm(l32);
-      const unsigned char* krow = ks + j * 256;
-      const int sw = swz_k(j);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + (((2 * st + half) ^ sw) & 15) * 16);
+    for (int st = 0; st < 8; ++st) {
+      const int off = (((2 * st + half) ^ ksw) & 15) * 16;
+#pragma unroll
+      for (int kt = 0; kt < T::kKeyTiles; ++kt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + kt * 32 * 256 + off);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kt], 0, 0, 0);
       }
     }
+    barrier_raw();            // every wave has read K(it)
+    const int nx = next_valid(it + 1);
+    if (nx < end) issue_k(col_idx[nx]);
 
-    // ---- online softmax (one query per lane; keys split over lane ^ 32)
+    // ---- online softmax (one query per lane, keys split over lane ^ 32)
     float mx = s[0][0];
 #pragma unroll
     for (int kt = 0; kt < T::kKeyTiles; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float neg_m = -m_new;
+    const float m_blk = pair_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const float neg_m = -m_run;
     float rs = 0.0f;
     bf16x8_t pb[T::kKeyTiles][2];
 #pragma unroll
@@ -217,34 +301,31 @@ __global__ void __launch_bounds__(BT * 2) attend_fwd_kernel(AttendParams p) {
         rs += e;
         pb[kt][r >> 3][r & 7] = (__bf16)e;
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    l_run += rs;
+
+    if (nx < end) wait_vmcnt<8>(); else wait_vmcnt<0>();   // V(it) landed
+    barrier_raw();
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = 32 * dt + l32;
-      const unsigned char* vrow = vt + d * (BT * 2);
-      const int sw = swz_v(d);
+    for (int kt = 0; kt < T::kKeyTiles; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < T::kKeyTiles; ++kt)
+      for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int x = 4 * kt + 2 * half + s2;
-          const bf16x8_t a =
-              *reinterpret_cast<const bf16x8_t*>(vrow + ((x ^ sw) & (T::kVChunks - 1)) * 16);
+        for (int dt = 0; dt < 4; ++dt) {
+          const int off = (((4 * dt + vchunk_lo) ^ vsw) & 15) * 16;
+          const unsigned char* base = vrow + (32 * kt + 8 * s2) * 256 + off;
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base));
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 4 * 256));
+          const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][s2], o[dt], 0, 0, 0);
         }
-    }
+      }
     it = nx;
   }
 
   // ---- epilogue: normalise, round to bf16, store; LSE
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   uint16_t* orow = p.o + (int64_t)b * p.o_sb + qtok * p.o_ss + (int64_t)h * p.o_sh;
 #pragma unroll

@@ -149,6 +149,12 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   if (!d_row_ptr) return fail(LCSA_ERR_NULL, "lcsa_attend: row_ptr is NULL");
   if (nnz < 0) return fail(LCSA_ERR_INVALID, "lcsa_attend: nnz %lld < 0", (long long)nnz);
   if (nnz > 0 && !d_col_idx) return fail(LCSA_ERR_NULL, "lcsa_attend: col_idx is NULL");
+  if (nnz >= INT32_MAX)
+    return fail(LCSA_ERR_SHAPE, "lcsa_attend: nnz %lld exceeds int32 CSR", (long long)nnz);
+  // The kernel addresses K/V rows inside one block with 32-bit byte offsets.
+  const int64_t in_block = (static_cast<int64_t>(in.block_h - 1) * plan->desc.grid_w + in.block_w) * 2;
+  if (in_block * k->stride_s >= INT32_MAX || in_block * v->stride_s >= INT32_MAX)
+    return fail(LCSA_ERR_SHAPE, "lcsa_attend: token stride too large for one key block");
   if ((st = lcsa::check_device())) return st;
 
   lcsa::AttendParams ap;
