@@ -115,21 +115,24 @@ lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   if ((st = lcsa::check_device())) return st;
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  lcsa::PoolKParams pk;
-  pk.g = lcsa::make_geom(plan);
-  pk.k = lcsa::make_view(k);
-  pk.kbar_t = static_cast<double*>(d_workspace);
-  hipError_t e = lcsa::launch_pool_k(pk, plan->desc.batch, in.block_tokens, s);
-  if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "pool_k launch: %s", hipGetErrorString(e));
+  const size_t qbar_bytes = static_cast<size_t>(in.rows) * 128 * sizeof(double);
+  lcsa::PoolParams pp;
+  pp.g = lcsa::make_geom(plan);
+  pp.q = lcsa::make_view(q);
+  pp.k = lcsa::make_view(k);
+  pp.qbar = static_cast<double*>(d_workspace);
+  pp.kbar_t = reinterpret_cast<double*>(static_cast<char*>(d_workspace) + qbar_bytes);
+  hipError_t e = lcsa::launch_pool(pp, plan->desc.batch, in.block_tokens, s);
+  if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "pool launch: %s", hipGetErrorString(e));
 
   lcsa::SelectParams sp;
-  sp.g = pk.g;
-  sp.q = lcsa::make_view(q);
-  sp.kbar_t = pk.kbar_t;
+  sp.g = pp.g;
+  sp.qbar = pp.qbar;
+  sp.kbar_t = pp.kbar_t;
   sp.row_ptr = d_row_ptr;
   sp.col_idx = d_col_idx;
   sp.scores = d_scores;
-  e = lcsa::launch_select(sp, plan->desc.batch, in.block_tokens, s);
+  e = lcsa::launch_select(sp, plan->desc.batch, in.max_window, s);
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "select launch: %s", hipGetErrorString(e));
   return LCSA_OK;
 }

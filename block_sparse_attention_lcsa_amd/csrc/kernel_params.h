@@ -23,15 +23,16 @@ struct View {
   int64_t sb, ss, sh;    // strides in elements
 };
 
-struct PoolKParams {
+struct PoolParams {
   GridGeom g;
-  View k;
-  double* kbar_t;  // [B][H][128][NKB]
+  View q, k;
+  double* qbar;          // [B][H][NQB][128]
+  double* kbar_t;        // [B][H][128][NKB]
 };
 
 struct SelectParams {
   GridGeom g;
-  View q;
+  const double* qbar;    // [B][H][NQB][128]
   const double* kbar_t;  // [B][H][128][NKB]
   int32_t* row_ptr;
   int32_t* col_idx;

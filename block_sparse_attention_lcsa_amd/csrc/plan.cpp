@@ -191,9 +191,10 @@ lcsa_status lcsa_plan_create(const lcsa_desc* d, lcsa_plan_t* out) {
   in.max_window = mxw;
   in.nnz = nnz;
   in.useful_flops = 4.0 * 128.0 * in.block_tokens * in.block_tokens * static_cast<double>(nnz);
-  // Workspace: pooled K as float64, transposed per (b, h): [B][H][128][NKB].
-  in.select_workspace_bytes =
-      static_cast<uint64_t>(d->batch) * d->heads * 128ull * static_cast<uint64_t>(nkb) * 8ull;
+  // Workspace: pooled Q [B][H][NQB][128] then pooled K transposed per
+  // (b, h) [B][H][128][NKB], both float64.
+  in.select_workspace_bytes = static_cast<uint64_t>(d->batch) * d->heads * 128ull *
+                              static_cast<uint64_t>(nqb + nkb) * 8ull;
 
   try {
     p->row_ptr.resize(static_cast<size_t>(rows) + 1);

@@ -1,6 +1,11 @@
-// Block selection kernels for gfx950: mean-pool K per key block, then per
-// (batch, head, spatial block position) mean-pool Q for every query frame,
-// score the window's pooled keys, keep the top k and emit the CSR block mask.
+// Block selection kernels for gfx950.
+//
+//  pool_kernel    mean of every query block of Q and key block of K, per head
+//                 (float64 sums of the bf16 values).
+//  select_kernel  one wave per CSR row (batch, head, query block): score the
+//                 pooled query against every pooled key block of its spatial
+//                 window, find the k-th best score, emit the kept blocks in
+//                 ascending order.
 //
 // Pooling and mask selection are the "attention glue" of the FlashVSR Hopper
 // PR page ("What Was Actually Slow"), with the mask emitted as CSR ("Rebuild
@@ -9,10 +14,16 @@
 // FlashVSR summary, "How it works", item 2; local_range on the FlashVSR
 // Inference skill page, "Non-Negotiable Streaming Contract").
 //
-// Arithmetic: block sums and scores are float64.  A bf16 value has 8
-// significant bits, so a sum of 128 of them is exact in float64 for any
-// practical value range; pooled vectors are therefore order-independent and
-// the ranking differs from an exact one only at score gaps of ~1e-16.
+// Arithmetic: a bf16 value has 8 significant bits, so the float64 sum of a
+// block's 64 or 128 values is exact for any practical value range; pooled
+// vectors are order-independent and scores are float64 dot products, so the
+// ranking differs from an exact one only at score gaps of ~1e-16 relative.
+//
+// Top-k: scores map to order-preserving 64-bit keys; the k-th largest key is
+// found by deciding its bits from the top, each bit by one wave-wide count
+// (ballot + popcount) of the keys at or above the trial value.  Keys above
+// it are kept; keys equal to it are kept in ascending block order until k
+// are kept (ties go to the lower block index).
 
 #include <hip/hip_runtime.h>
 
@@ -23,7 +34,9 @@
 namespace lcsa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kPoolThreads = 256;
+constexpr int kSelectWaves = 4;
+constexpr int kMaxPerLane = kMaxWindow / 64;   // window candidates per lane
 
 __device__ inline double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ inline double bf16_hi(uint32_t w) { return (double)__uint_as_float(w & 0xffff0000u); }
@@ -35,19 +48,27 @@ __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, 
   return ((int64_t)t * g.grid_h + y) * g.grid_w + x;
 }
 
-// Sum of one block's rows of one head into red[16][128]: thread (c, tg) adds
-// 8 channels 8c..8c+7 of tokens tg, tg+16, ...
+// grid (NQB + NKB, heads, batch): x < NQB pools query block x, otherwise key
+// block x - NQB.  Thread (c, tg) sums channels 8c..8c+7 of tokens tg, tg+16..
 template <int BT>
-__device__ inline void block_sum_partial(const GridGeom& g, const uint16_t* base, int64_t ss,
-                                         int t, int by, int bx, double* red) {
-  const int tid = threadIdx.x;
-  const int c = tid & 15, tg = tid >> 4;
+__global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
+  __shared__ double red[16 * 128];
+  const GridGeom& g = p.g;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const bool is_q = (int)blockIdx.x < g.nqb;
+  const int blk = is_q ? (int)blockIdx.x : (int)blockIdx.x - g.nqb;
+  const View& x = is_q ? p.q : p.k;
+  const int t = blk / g.nbf, pos = blk - t * g.nbf;
+  const int by = pos / g.nbw, bx = pos - by * g.nbw;
+  const uint16_t* base = x.data + (int64_t)b * x.sb + (int64_t)h * x.sh;
+  const int tid = threadIdx.x, c = tid & 15, tg = tid >> 4;
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 #pragma unroll
-  for (int j = tg; j < BT; j += 16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(base + block_token(g, t, by, bx, j) * ss + c * 8);
+  for (int i = 0; i < BT / 16; ++i) {
+    const int j = tg + 16 * i;
+    const uint4 w = *reinterpret_cast<const uint4*>(base + block_token(g, t, by, bx, j) * x.ss + c * 8);
     acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
     acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
     acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
@@ -55,24 +76,17 @@ __device__ inline void block_sum_partial(const GridGeom& g, const uint16_t* base
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[tg * 128 + c * 8 + e] = acc[e];
-}
-
-template <int BT>
-__global__ void __launch_bounds__(kThreads) pool_k_kernel(PoolKParams p) {
-  __shared__ double red[16 * 128];
-  const GridGeom& g = p.g;
-  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t = kb / g.nbf, pos = kb - t * g.nbf;
-  const int by = pos / g.nbw, bx = pos - by * g.nbw;
-  const uint16_t* base = p.k.data + (int64_t)b * p.k.sb + (int64_t)h * p.k.sh;
-  block_sum_partial<BT>(g, base, p.k.ss, t, by, bx, red);
   __syncthreads();
-  const int d = threadIdx.x;
-  if (d < 128) {
+  if (tid < 128) {
     double s = 0.0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) s += red[q * 128 + d];
-    p.kbar_t[(((int64_t)b * g.heads + h) * 128 + d) * g.nkb + kb] = s * (1.0 / BT);
+    for (int q = 0; q < 16; ++q) s += red[q * 128 + tid];
+    s *= (1.0 / BT);
+    const int64_t bh = (int64_t)b * g.heads + h;
+    if (is_q)
+      p.qbar[(bh * g.nqb + blk) * 128 + tid] = s;
+    else
+      p.kbar_t[(bh * 128 + tid) * g.nkb + blk] = s;
   }
 }
 
@@ -103,173 +117,183 @@ __device__ inline int window_kb(const GridGeom& g, const WindowBox& w, int e) {
   return t * g.nbf + (w.y0 + yy) * g.nbw + (w.x0 + xx);
 }
 
-// Candidate x ranks before y: higher score, then lower index; padding last.
-__device__ inline bool ranks_before(const double* sc, int n, int x, int y) {
-  if (x >= n) return false;
-  if (y >= n) return true;
-  const double sx = sc[x], sy = sc[y];
-  return sx > sy || (sx == sy && x < y);
+// Order-preserving key of a double (larger score -> larger key; -0 == +0).
+__device__ inline uint64_t order_key(double s) {
+  const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <int BT>
-__global__ void __launch_bounds__(kThreads) select_kernel(SelectParams p) {
-  // Region A is the pooling reduction buffer first, then the score table.
-  __shared__ double region_a[kSelectFrames * kMaxWindow];
-  __shared__ double qbar[kSelectFrames * 128];
-  __shared__ uint16_t order[kMaxWindow];
-  __shared__ uint8_t flag[kMaxWindow];
-  __shared__ int s_sum[2];
+__device__ inline int wave_count(bool pred) {
+  return __popcll(__builtin_amdgcn_ballot_w64(pred));
+}
 
+template <int M>
+__device__ void select_row(const SelectParams& p, const WindowBox& w, int b, int h, int tq, int pos,
+                           double* qs) {
   const GridGeom& g = p.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pos = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)b * g.heads + h;
+  const int qb = tq * g.nbf + pos;
+  const int64_t row = bh * g.nqb + qb;
+
+  // Pooled query of this row -> LDS (read back as broadcasts).
+  const double* qsrc = p.qbar + row * 128;
+  qs[lane] = qsrc[lane];
+  qs[lane + 64] = qsrc[lane + 64];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+  // Lane-per-candidate float64 scores: candidate e = lane + 64 j.
+  int kb[M];
+  bool valid[M];
+  double acc[M];
+  const double* kcol = p.kbar_t + bh * 128 * g.nkb;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const int e = lane + 64 * j;
+    valid[j] = e < w.n;
+    kb[j] = valid[j] ? window_kb(g, w, e) : 0;
+    acc[j] = 0.0;
+  }
+#pragma unroll 4
+  for (int d = 0; d < 128; ++d) {
+    const double qd = qs[d];
+    const double* kd = kcol + (int64_t)d * g.nkb;
+#pragma unroll
+    for (int j = 0; j < M; ++j) acc[j] = fma(qd, kd[kb[j]], acc[j]);
+  }
+
+  if (p.scores) {  // every key block written once: -inf outside the window
+    double* srow = p.scores + row * g.nkb;
+    for (int x = lane; x < g.nkb; x += 64) {
+      const int xt = x / g.nbf, xp = x - xt * g.nbf;
+      const int xy = xp / g.nbw, xx = xp - xy * g.nbw;
+      if (xy < w.y0 || xy > w.y1 || xx < w.x0 || xx > w.x1) srow[x] = -__builtin_huge_val();
+    }
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (valid[j]) srow[kb[j]] = acc[j];
+  }
+
+  // CSR offset of this row: rows run (b, h, frame, position); every frame
+  // holds the same per-position counts min(k, |window(position)|).
+  int lt = 0, all = 0;
+  for (int q = lane; q < g.nbf; q += 64) {
+    const int qy = q / g.nbw, qx = q - qy * g.nbw;
+    const int c = min(g.k, window_box(g, qy, qx).n);
+    all += c;
+    lt += q < pos ? c : 0;
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    lt += __shfl_xor(lt, m);
+    all += __shfl_xor(all, m);
+  }
+  const int keep = min(g.k, w.n);
+  const int64_t off = (bh * g.q_frames + tq) * (int64_t)all + lt;
+  if (lane == 0) {
+    p.row_ptr[row + 1] = (int32_t)(off + keep);
+    if (row == 0) p.row_ptr[0] = 0;
+  }
+
+  bool sel[M];
+  if (keep >= w.n) {
+#pragma unroll
+    for (int j = 0; j < M; ++j) sel[j] = valid[j];
+  } else {
+    uint64_t key[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) key[j] = valid[j] ? order_key(acc[j]) : 0ull;
+    // Largest T with #{key >= T} >= keep, decided bit by bit from the top.
+    // Invalid lanes hold key 0, which never reaches a trial value > 0.
+    uint64_t t = 0;
+    bool exact = false;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t trial = t | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < M; ++j) cnt += wave_count(key[j] >= trial);
+      if (cnt >= keep) t = trial;
+      if (cnt == keep) {  // the set {key >= trial} is exactly the top keep
+        exact = true;
+        break;
+      }
+    }
+    if (exact) {
+#pragma unroll
+      for (int j = 0; j < M; ++j) sel[j] = valid[j] && key[j] >= t;
+    } else {
+      // t is the keep-th largest key; keys == t are admitted by index.
+      int need = keep;
+#pragma unroll
+      for (int j = 0; j < M; ++j) need -= wave_count(valid[j] && key[j] > t);
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const bool tie = valid[j] && key[j] == t;
+        const uint64_t tm = __builtin_amdgcn_ballot_w64(tie);
+        const int rank = __popcll(tm & below);
+        sel[j] = (valid[j] && key[j] > t) || (tie && rank < need);
+        need -= __popcll(tm);
+        need = need < 0 ? 0 : need;
+      }
+    }
+  }
+
+  // Emit kept blocks in ascending candidate (= key block) order.
+  const uint64_t below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(sel[j]);
+    if (sel[j]) p.col_idx[off + base + __popcll(m & below)] = kb[j];
+    base += __popcll(m);
+  }
+}
+
+// grid (ceil(q_frames / kSelectWaves), NBF, heads * batch); wave w of a
+// workgroup handles query frame blockIdx.x * kSelectWaves + w at spatial
+// position blockIdx.y.  The waves of a workgroup share one window, so their
+// pooled-key reads hit the same cache lines.
+template <int M>
+__global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams p) {
+  __shared__ double qshare[kSelectWaves][128];
+  const GridGeom& g = p.g;
+  const int wave = threadIdx.x >> 6;
+  const int tq = blockIdx.x * kSelectWaves + wave;
+  const int pos = blockIdx.y;
+  const int h = blockIdx.z % g.heads, b = blockIdx.z / g.heads;
+  if (tq >= g.q_frames) return;
   const int by = pos / g.nbw, bx = pos - by * g.nbw;
   const WindowBox w = window_box(g, by, bx);
-  const int keep = min(g.k, w.n);
-
-  // Offset of this position inside one frame's CSR rows, and the per-frame
-  // total: sums of min(k, |window|) over spatial positions.
-  if (tid < 2) s_sum[tid] = 0;
-  __syncthreads();
-  {
-    int lt = 0, all = 0;
-    for (int q = tid; q < g.nbf; q += kThreads) {
-      const int qy = q / g.nbw, qx = q - qy * g.nbw;
-      const WindowBox wq = window_box(g, qy, qx);
-      const int c = min(g.k, wq.n);
-      all += c;
-      if (q < pos) lt += c;
-    }
-    atomicAdd(&s_sum[0], lt);
-    atomicAdd(&s_sum[1], all);
-  }
-
-  const uint16_t* qbase = p.q.data + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
-  const double* kcol = p.kbar_t + ((int64_t)b * g.heads + h) * 128 * g.nkb;
-
-  for (int tq0 = 0; tq0 < g.q_frames; tq0 += kSelectFrames) {
-    const int ntq = min(kSelectFrames, g.q_frames - tq0);
-    // ---- pool the query block of each frame
-    for (int u = 0; u < ntq; ++u) {
-      __syncthreads();
-      block_sum_partial<BT>(g, qbase, p.q.ss, tq0 + u, by, bx, region_a);
-      __syncthreads();
-      if (tid < 128) {
-        double s = 0.0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) s += region_a[q * 128 + tid];
-        qbar[u * 128 + tid] = s * (1.0 / BT);
-      }
-    }
-    __syncthreads();
-    // ---- score every window candidate against every pooled query
-    for (int e = tid; e < w.n; e += kThreads) {
-      const int kb = window_kb(g, w, e);
-      double acc[kSelectFrames];
-#pragma unroll
-      for (int u = 0; u < kSelectFrames; ++u) acc[u] = 0.0;
-      for (int d = 0; d < 128; ++d) {
-        const double kv = kcol[(int64_t)d * g.nkb + kb];
-#pragma unroll
-        for (int u = 0; u < kSelectFrames; ++u)
-          if (u < ntq) acc[u] = fma(qbar[u * 128 + d], kv, acc[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kSelectFrames; ++u)
-        if (u < ntq) region_a[u * kMaxWindow + e] = acc[u];
-    }
-    __syncthreads();
-    if (p.scores) {
-      for (int u = 0; u < ntq; ++u) {
-        const int qb = (tq0 + u) * g.nbf + pos;
-        double* srow = p.scores + (((int64_t)b * g.heads + h) * g.nqb + qb) * g.nkb;
-        for (int kb = tid; kb < g.nkb; kb += kThreads) {
-          const int kt = kb / g.nbf, kp = kb - kt * g.nbf;
-          const int ky = kp / g.nbw, kx = kp - ky * g.nbw;
-          double v = -__builtin_huge_val();
-          if (ky >= w.y0 && ky <= w.y1 && kx >= w.x0 && kx <= w.x1)
-            v = region_a[u * kMaxWindow + (kt * w.nr + (ky - w.y0)) * w.nc + (kx - w.x0)];
-          srow[kb] = v;
-        }
-      }
-    }
-    // ---- top-k per query frame, emitted ascending
-    const int prefix = s_sum[0], frame_total = s_sum[1];
-    for (int u = 0; u < ntq; ++u) {
-      const int tq = tq0 + u;
-      const int64_t row = ((int64_t)b * g.heads + h) * g.nqb + (int64_t)tq * g.nbf + pos;
-      const int64_t off =
-          (((int64_t)b * g.heads + h) * g.q_frames + tq) * (int64_t)frame_total + prefix;
-      if (tid == 0) {
-        p.row_ptr[row + 1] = (int32_t)(off + keep);
-        if (row == 0) p.row_ptr[0] = 0;
-      }
-      const double* sc = region_a + u * kMaxWindow;
-      if (keep < w.n) {
-        int n2 = 1;
-        while (n2 < w.n) n2 <<= 1;
-        for (int i = tid; i < n2; i += kThreads) order[i] = (uint16_t)i;
-        __syncthreads();
-        for (int size = 2; size <= n2; size <<= 1) {
-          for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < n2; i += kThreads) {
-              const int j = i ^ stride;
-              if (j > i) {
-                const int a = order[i], c = order[j];
-                const bool first_half_best = (i & size) == 0;
-                const bool swap = first_half_best ? ranks_before(sc, w.n, c, a)
-                                                  : ranks_before(sc, w.n, a, c);
-                if (swap) {
-                  order[i] = (uint16_t)c;
-                  order[j] = (uint16_t)a;
-                }
-              }
-            }
-            __syncthreads();
-          }
-        }
-        for (int i = tid; i < w.n; i += kThreads) flag[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < keep; i += kThreads) flag[order[i]] = 1;
-      } else {
-        for (int i = tid; i < w.n; i += kThreads) flag[i] = 1;
-      }
-      __syncthreads();
-      if (wave == 0) {
-        int base = 0;
-        for (int c0 = 0; c0 < w.n; c0 += 64) {
-          const int e = c0 + lane;
-          const bool f = e < w.n && flag[e];
-          const uint64_t m = __ballot(f);
-          if (f) {
-            const int before = __popcll(m & ((1ull << lane) - 1ull));
-            p.col_idx[off + base + before] = window_kb(g, w, e);
-          }
-          base += __popcll(m);
-        }
-      }
-      __syncthreads();
-    }
-  }
+  select_row<M>(p, w, b, h, tq, pos, qshare[wave]);
 }
 
 }  // namespace
 
-hipError_t launch_pool_k(const PoolKParams& p, int batch, int block_tokens, hipStream_t stream) {
-  const dim3 grid(p.g.nkb, p.g.heads, batch);
+hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStream_t stream) {
+  const dim3 grid(p.g.nqb + p.g.nkb, p.g.heads, batch);
   if (block_tokens == 128)
-    hipLaunchKernelGGL(pool_k_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(pool_k_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectParams& p, int batch, int block_tokens, hipStream_t stream) {
-  const dim3 grid(p.g.nbf, p.g.heads, batch);
-  if (block_tokens == 128)
-    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kThreads), 0, stream, p);
+hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipStream_t stream) {
+  const dim3 grid((p.g.q_frames + kSelectWaves - 1) / kSelectWaves, p.g.nbf, p.g.heads * batch);
+  const dim3 block(kSelectWaves * 64);
+  // Candidates per lane, rounded up to a compiled width.
+  const int m = (max_window + 63) / 64;
+  if (m <= 1)
+    hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, stream, p);
+  else if (m <= 4)
+    hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, stream, p);
+  else if (m <= 8)
+    hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, stream, p);
+  else if (m <= 12)
+    hipLaunchKernelGGL(select_kernel<12>, grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(select_kernel<kMaxPerLane>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
