@@ -10,8 +10,10 @@ seeded synthetic bf16 inputs resident in HBM before timing starts.
 Prints ONE JSON line.  value = useful attention TFLOP/s of the whole step
 (useful FLOP = 4 * 128 * 128 * 128 per selected block pair; skipped blocks do
 not count), ms_per_step = select+attend ms per chunk.  roofline = the attend
-kernel (MFMA-bound) timed with HIP events on its stream; cpu_baseline = the
-float64 CPU oracle on a bounded sample of the same workload.
+kernel (MFMA-bound) timed with HIP events on its stream; select_roofline =
+the select entry point (pool + select kernels) against HBM bandwidth;
+cpu_baseline = the float64 CPU oracle on a bounded sample of the same
+workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
@@ -181,6 +183,11 @@ def main():
     sel_avg = float(np.mean(sel_ms))
     step_ms = max(wall_ms, gpu_ms)
     achieved = flops / (att_avg * 1e-3) / 1e12
+    # select: algorithmic HBM bytes = Q and K read once (bf16) + the CSR
+    # written (row_ptr and col_idx, int32)
+    sel_bytes = (2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + info["kv_tokens"])
+                 + 4 * (info["rows"] + 1 + info["nnz"]))
+    sel_gbs = sel_bytes / (sel_avg * 1e-3) / 1e9
 
     res = {
         "metric": "LCSA attend useful TFLOP/s + fraction of bf16 MFMA peak; select+attend ms/chunk",
@@ -216,6 +223,14 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": _traffic(name),
+        },
+        "select_roofline": {
+            "bound": "hbm",
+            "achieved": sel_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": sel_gbs / PEAK_HBM_GBS,
+            "bytes": sel_bytes,
         },
         "device": torch.cuda.get_device_name(0),
     }

@@ -29,7 +29,7 @@ def lib_path() -> str:
 
 if not os.path.exists(lib_path()):
     raise ImportError(
-        "liblcsa.so is not built; run `python -m block_sparse_attention_lcsa_amd.build_lib` "
+        "liblcsa.so is not built; run `python block_sparse_attention_lcsa_amd/build_lib.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 
 _lib = ctypes.CDLL(lib_path())

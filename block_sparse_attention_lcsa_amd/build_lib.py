@@ -1,6 +1,7 @@
 """Build liblcsa.so (host plan + gfx950 kernels) in-tree with hipcc.
 
-Usage: python -m block_sparse_attention_lcsa_amd.build_lib [--verbose]
+Usage: python block_sparse_attention_lcsa_amd/build_lib.py [--verbose]
+(run by path: importing the package needs the built library)
 """
 from __future__ import annotations
 

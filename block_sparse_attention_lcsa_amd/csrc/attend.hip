@@ -43,6 +43,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -69,6 +71,11 @@ __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, 
   const int y = by * g.block_h + (j >> g.log2_bw);
   const int x = bx * g.block_w + (j & (g.block_w - 1));
   return ((int64_t)t * g.grid_h + y) * g.grid_w + x;
+}
+
+// n / d for 0 <= n < 2^31 with a host-computed magic multiplier.
+__device__ inline int fast_div(int n, uint32_t m, uint32_t shift) {
+  return (int)(((uint64_t)(uint32_t)n * m) >> shift);
 }
 
 // Workgroup barrier that completes this wave's own LDS reads (lgkmcnt) but
@@ -195,8 +202,8 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k.data + (int64_t)b * p.k.sb + (int64_t)h * p.k.sh);
   const char* vbase = reinterpret_cast<const char*>(p.v.data + (int64_t)b * p.v.sb + (int64_t)h * p.v.sh);
   auto block_offset = [&](int kb, int64_t ss2) {
-    const int t = kb / g.nbf, ps = kb - t * g.nbf;
-    const int kby = ps / g.nbw, kbx = ps - kby * g.nbw;
+    const int t = fast_div(kb, g.nbf_m, g.nbf_s), ps = kb - t * g.nbf;
+    const int kby = fast_div(ps, g.nbw_m, g.nbw_s), kbx = ps - kby * g.nbw;
     const int64_t tok0 = ((int64_t)t * g.grid_h + (int64_t)kby * g.block_h) * g.grid_w + (int64_t)kbx * g.block_w;
     return tok0 * ss2;
   };
@@ -254,19 +261,20 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     barrier_raw();            // ... everyone's; V buffer free (PV of it-1 done)
     issue_v(kb);
 
-    // ---- S^T = K Q^T
+    // ---- S^T = K Q^T (the first step starts from a zero accumulator)
     f32x16_t s[T::kKeyTiles];
-#pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int off = (((2 * st + half) ^ ksw) & 15) * 16;
 #pragma unroll
       for (int kt = 0; kt < T::kKeyTiles; ++kt) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + kt * 32 * 256 + off);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kt], 0, 0, 0);
+        if (st == 0) {
+          const f32x16_t zero = {};
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0], zero, 0, 0, 0);
+        } else {
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kt], 0, 0, 0);
+        }
       }
     }
     barrier_raw();            // every wave has read K(it)
@@ -274,11 +282,17 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     if (nx < end) issue_k(col_idx[nx]);
 
     // ---- online softmax (one query per lane, keys split over lane ^ 32)
-    float mx = s[0][0];
+    // Independent max chains per key tile keep the reduction short.
+    float mt[T::kKeyTiles];
 #pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt)
+    for (int kt = 0; kt < T::kKeyTiles; ++kt) {
+      mt[kt] = fmaxf(s[kt][0], s[kt][1]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      for (int r = 2; r < 16; ++r) mt[kt] = fmaxf(mt[kt], s[kt][r]);
+    }
+    float mx = mt[0];
+#pragma unroll
+    for (int kt = 1; kt < T::kKeyTiles; ++kt) mx = fmaxf(mx, mt[kt]);
     const float m_blk = pair_max(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_run, m_blk);
@@ -291,17 +305,32 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
     const float neg_m = -m_run;
-    float rs = 0.0f;
+    // P = exp2(S * scale*log2(e) - m) rounded to bf16 pairs; the row sum adds
+    // exactly these rounded values (dot with (1, 1)), one chain per key tile.
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     bf16x8_t pb[T::kKeyTiles][2];
+    float rs[T::kKeyTiles];
 #pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt)
+    for (int kt = 0; kt < T::kKeyTiles; ++kt) {
+      rs[kt] = 0.0f;
+      bf16x2_t pp[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], sl2, neg_m));
-        rs += e;
-        pb[kt][r >> 3][r & 7] = (__bf16)e;
+      for (int r2 = 0; r2 < 8; ++r2) {
+        f32x2_t e;
+        e[0] = __builtin_amdgcn_exp2f(fmaf(s[kt][2 * r2], sl2, neg_m));
+        e[1] = __builtin_amdgcn_exp2f(fmaf(s[kt][2 * r2 + 1], sl2, neg_m));
+        pp[r2] = __builtin_convertvector(e, bf16x2_t);
+        rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(pp[r2], ones, rs[kt], false);
       }
-    l_run += rs;
+      pb[kt][0] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                          0, 1, 2, 3, 4, 5, 6, 7);
+      pb[kt][1] = __builtin_shufflevector(__builtin_shufflevector(pp[4], pp[5], 0, 1, 2, 3),
+                                          __builtin_shufflevector(pp[6], pp[7], 0, 1, 2, 3),
+                                          0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int kt = 0; kt < T::kKeyTiles; ++kt) l_run += rs[kt];
 
     if (nx < end) wait_vmcnt<8>(); else wait_vmcnt<0>();   // V(it) landed
     barrier_raw();

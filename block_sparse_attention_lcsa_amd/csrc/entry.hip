@@ -54,6 +54,16 @@ lcsa_status check_view(const char* name, const lcsa_tensor* t, int64_t tokens, i
   return LCSA_OK;
 }
 
+// Magic multiplier for n / d with 0 <= n < 2^31 and d >= 1 (round-up
+// method): l = ceil(log2 d), m = floor(2^(31+l) / d) + 1 < 2^32, and
+// n / d == (n * m) >> (31 + l) because m * d - 2^(31+l) <= d <= 2^l.
+void magic_div(uint32_t d, uint32_t* m, uint32_t* shift) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  *m = static_cast<uint32_t>(((1ull << (31 + l)) / d) + 1);
+  *shift = 31 + l;
+}
+
 GridGeom make_geom(const lcsa_plan_s* p) {
   const lcsa_plan_info& in = p->info;
   GridGeom g;
@@ -74,6 +84,8 @@ GridGeom make_geom(const lcsa_plan_s* p) {
   g.half = in.half_window;
   g.k = in.k;
   g.q_tokens = in.q_tokens;
+  magic_div(static_cast<uint32_t>(g.nbf), &g.nbf_m, &g.nbf_s);
+  magic_div(static_cast<uint32_t>(g.nbw), &g.nbw_m, &g.nbw_s);
   return g;
 }
 

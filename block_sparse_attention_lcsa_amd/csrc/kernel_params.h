@@ -16,6 +16,9 @@ struct GridGeom {
   int32_t half;                       // window half-width in blocks
   int32_t k;                          // kept-block budget
   int64_t q_tokens;
+  // Division by nbf and nbw as a multiply and shift (exact for n < 2^31):
+  // n / d == (n * m) >> s with a 64-bit product.
+  uint32_t nbf_m, nbf_s, nbw_m, nbw_s;
 };
 
 struct View {
@@ -48,7 +51,7 @@ struct AttendParams {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int64_t nnz;
-  int64_t rows;
+  int64_t rows;          // CSR rows = workgroups
   float scale_log2;      // softmax scale * log2(e)
 };
 
