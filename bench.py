@@ -146,6 +146,7 @@ def main():
     info = plan.info
     flops = float(info["useful_flops"])
     ws = torch.empty(max(int(info["select_workspace_bytes"]), 256), dtype=torch.uint8, device=dev)
+    att_ws = torch.empty(int(info["attend_workspace_bytes"]), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
 
@@ -156,7 +157,7 @@ def main():
         rp, ci = lcsa.select(p, q, k, workspace=ws)
         if ev:
             ev[1].record(stream)
-        lcsa.attend(p, q, k, v, rp, ci, out=out)
+        lcsa.attend(p, q, k, v, rp, ci, out=out, workspace=att_ws)
         if ev:
             ev[2].record(stream)
 

@@ -73,7 +73,8 @@ class LcsaPlanInfo(ctypes.Structure):
                 ("min_window", ctypes.c_int32), ("max_window", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("nnz", ctypes.c_int64),
                 ("q_tokens", ctypes.c_int64), ("kv_tokens", ctypes.c_int64),
-                ("select_workspace_bytes", ctypes.c_uint64), ("scale", ctypes.c_double),
+                ("select_workspace_bytes", ctypes.c_uint64),
+                ("attend_workspace_bytes", ctypes.c_uint64), ("scale", ctypes.c_double),
                 ("useful_flops", ctypes.c_double)]
 
 
@@ -94,7 +95,7 @@ _lib.lcsa_select.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(Lcsa
 _lib.lcsa_select.restype = ctypes.c_int32
 _lib.lcsa_attend.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
                              ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_int64,
-                             ctypes.POINTER(LcsaTensor), _P, _P]
+                             ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_size_t, _P]
 _lib.lcsa_attend.restype = ctypes.c_int32
 _lib.lcsa_status_string.argtypes = [ctypes.c_int32]
 _lib.lcsa_status_string.restype = ctypes.c_char_p
@@ -231,8 +232,13 @@ def select(plan: Plan, q, k, return_scores: bool = False, workspace=None, stream
 
 
 def attend(plan: Plan, q, k, v, row_ptr, col_idx, out=None, return_lse: bool = False,
-           stream=None):
-    """Block-sparse attention forward over the CSR (row_ptr, col_idx)."""
+           workspace=None, split_tail: bool = True, stream=None):
+    """Block-sparse attention forward over the CSR (row_ptr, col_idx).
+
+    With split_tail (default) a workspace of attend_workspace_bytes is used
+    (allocated here if not given) so that rows of a last, partly filled round
+    of workgroups are split and merged; split_tail=False runs every row as
+    one workgroup."""
     import torch
     _check_shape(q, plan, "q_tokens", "q")
     _check_shape(k, plan, "kv_tokens", "k")
@@ -252,11 +258,18 @@ def attend(plan: Plan, q, k, v, row_ptr, col_idx, out=None, return_lse: bool = F
         d = plan.desc
         lse = torch.empty((d["batch"], d["heads"], plan.info["q_tokens"]), dtype=torch.float32,
                           device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if split_tail:
+        if workspace is None:
+            workspace = torch.empty(int(plan.info["attend_workspace_bytes"]), dtype=torch.uint8,
+                                    device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     qv, kv, vv, ov = tensor_view(q), tensor_view(k), tensor_view(v), tensor_view(out)
     st = _lib.lcsa_attend(plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
                           row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else None,
                           col_idx.numel(), ctypes.byref(ov),
-                          lse.data_ptr() if lse is not None else None, _stream_ptr(q, stream))
+                          lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
+                          _stream_ptr(q, stream))
     _check(st, "lcsa_attend")
     if return_lse:
         return out, lse

@@ -23,9 +23,10 @@
 //    swizzle.  Operand A of V^T P^T is read with the LDS transpose read
 //    (ds_read_b64_tr_b16), which returns 4 keys of one channel per lane.
 //  * K and V buffers have separate lifetimes: V(i) streams in while S(i) and
-//    the softmax run, K(i+1) while the softmax and PV(i) run.  Barriers are
-//    raw s_barrier with explicit vmcnt waits, so in-flight tile loads are
-//    not drained at every barrier.
+//    the softmax run, K(i+1) while PV(i) runs; the loads of a tile are
+//    spread over the MFMA loop (one per step) instead of issued in a burst.
+//    Barriers are raw s_barrier with explicit vmcnt waits, so in-flight
+//    tile loads are not drained at every barrier.
 //  * Lazy rescale: the running max only moves when some lane's block max
 //    exceeds it by more than 2^8; exp2 arguments stay <= 8, and O and the row
 //    sum share the same stale reference, so the result is unchanged.
@@ -145,14 +146,23 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  // XCD-aware row order: workgroup ids go round-robin over the XCDs; give
-  // XCD x the contiguous row range [start_x, start_x + count_x).
-  int64_t row;
+  // Work item: workgroups [0, full_rows) take whole rows, in an XCD-aware
+  // order (workgroup ids go round-robin over the XCDs; XCD x gets the
+  // contiguous row range [start_x, start_x + count_x)); later workgroups
+  // take piece `piece` of a split row.
+  int64_t row, item = -1;
+  int piece = -1;
   {
-    const int64_t pid = blockIdx.x, n = p.rows;
-    const int64_t xcd = pid % kXcds, idx = pid / kXcds;
-    const int64_t per = n / kXcds, rem = n % kXcds;
-    row = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    const int64_t pid = blockIdx.x, n = p.full_rows;
+    if (pid < n) {
+      const int64_t xcd = pid % kXcds, idx = pid / kXcds;
+      const int64_t per = n / kXcds, rem = n % kXcds;
+      row = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    } else {
+      item = pid - n;
+      row = n + item / p.pieces;
+      piece = (int)(item % p.pieces);
+    }
   }
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;
@@ -183,6 +193,13 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   int start = row_ptr[row], end = row_ptr[row + 1];
   start = start < 0 ? 0 : (start > nnz ? nnz : start);
   end = end < start ? start : (end > nnz ? nnz : end);
+  if (piece >= 0) {
+    // consecutive parts of the row's CSR range
+    const int64_t len = end - start;
+    const int s0 = start + (int)(len * piece / p.pieces);
+    end = start + (int)(len * (piece + 1) / p.pieces);
+    start = s0;
+  }
   start = __builtin_amdgcn_readfirstlane(start);
   end = __builtin_amdgcn_readfirstlane(end);
 
@@ -209,16 +226,6 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   };
   const uint32_t k_lds_addr = lds_address(k_lds) + wave * 1024;
   const uint32_t v_lds_addr = lds_address(v_lds) + wave * 1024;
-  auto issue_k = [&](int kb) {
-    const char* src = kbase + block_offset(kb, row_stride_k);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(src, koff[i], k_lds_addr + i * T::kWaves * 1024);
-  };
-  auto issue_v = [&](int kb) {
-    const char* src = vbase + block_offset(kb, row_stride_v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(src, voff[i], v_lds_addr + i * T::kWaves * 1024);
-  };
   // Next CSR position >= i holding a valid key block (uniform; scalar loads).
   auto next_valid = [&](int i) {
     i = __builtin_amdgcn_readfirstlane(i);
@@ -253,19 +260,26 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   const float sl2 = p.scale_log2;
 
   int it = next_valid(start);
-  if (it < end) issue_k(col_idx[it]);
+  if (it < end) {   // K of the first block
+    const char* src = kbase + block_offset(col_idx[it], row_stride_k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(src, koff[i], k_lds_addr + i * T::kWaves * 1024);
+  }
 
   while (it < end) {
     const int kb = col_idx[it];
     wait_vmcnt<0>();          // K(it) landed (this wave's share)
     barrier_raw();            // ... everyone's; V buffer free (PV of it-1 done)
-    issue_v(kb);
+    // V(it) is issued one load per S step below, so the loads do not queue
+    // up in front of the MFMAs.
+    const char* vsrc = vbase + block_offset(kb, row_stride_v);
 
     // ---- S^T = K Q^T (the first step starts from a zero accumulator)
     f32x16_t s[T::kKeyTiles];
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int off = (((2 * st + half) ^ ksw) & 15) * 16;
+      dma16(vsrc, voff[st], v_lds_addr + st * T::kWaves * 1024);
 #pragma unroll
       for (int kt = 0; kt < T::kKeyTiles; ++kt) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + kt * 32 * 256 + off);
@@ -279,7 +293,10 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     }
     barrier_raw();            // every wave has read K(it)
     const int nx = next_valid(it + 1);
-    if (nx < end) issue_k(col_idx[nx]);
+    // K(nx) is issued one load per PV step below (after the V barrier, when
+    // every wave is done with K(it)); on the last block the current block is
+    // re-read instead, which keeps the loop body branch-free.
+    const char* ksrc = kbase + block_offset(col_idx[nx < end ? nx : it], row_stride_k);
 
     // ---- online softmax (one query per lane, keys split over lane ^ 32)
     // Independent max chains per key tile keep the reduction short.
@@ -332,7 +349,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
 #pragma unroll
     for (int kt = 0; kt < T::kKeyTiles; ++kt) l_run += rs[kt];
 
-    if (nx < end) wait_vmcnt<8>(); else wait_vmcnt<0>();   // V(it) landed
+    wait_vmcnt<0>();          // V(it) landed (the only loads in flight)
     barrier_raw();
 
     // ---- O^T += V^T P^T
@@ -340,6 +357,12 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     for (int kt = 0; kt < T::kKeyTiles; ++kt)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
+        // loads [j*L, j*L + L) of K(nx) at PV step j, L = 8 / steps
+        constexpr int kPvSteps = 2 * T::kKeyTiles, kPerStep = 8 / kPvSteps;
+        static_assert(kPerStep * kPvSteps == 8, "K loads spread evenly over PV steps");
+#pragma unroll
+        for (int i = (kt * 2 + s2) * kPerStep; i < (kt * 2 + s2 + 1) * kPerStep; ++i)
+          dma16(ksrc, koff[i], k_lds_addr + i * T::kWaves * 1024);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int off = (((4 * dt + vchunk_lo) ^ vsw) & 15) * 16;
@@ -352,9 +375,28 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
       }
     it = nx;
   }
+  wait_vmcnt<0>();            // no load may still target LDS when the workgroup retires
+
+  const float l_tot = pair_sum(l_run);
+  if (piece >= 0) {
+    // ---- split row: unnormalised O and (m, l) of this piece, in float32
+    float* op = p.part + (item * BT + qi) * 128;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 w = {o[dt][4 * a4 + 0], o[dt][4 * a4 + 1], o[dt][4 * a4 + 2], o[dt][4 * a4 + 3]};
+        *reinterpret_cast<float4*>(op + 32 * dt + 8 * a4 + 4 * half) = w;
+      }
+    if (half == 0) {
+      const int64_t items = (p.rows - p.full_rows) * p.pieces;
+      const float2 ml = {m_run, l_tot};
+      *reinterpret_cast<float2*>(p.part + items * BT * 128 + (item * BT + qi) * 2) = ml;
+    }
+    return;
+  }
 
   // ---- epilogue: normalise, round to bf16, store; LSE
-  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   uint16_t* orow = p.o + (int64_t)b * p.o_sb + qtok * p.o_ss + (int64_t)h * p.o_sh;
 #pragma unroll
@@ -377,16 +419,87 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   }
 }
 
+// Merge of split rows: one workgroup per split row, thread t handles query
+// t / 2 and channels 64 * (t % 2) .. +63.  Pieces hold O and the row sum
+// against their own reference m (log2 units); the merge rescales each to the
+// largest m.  A row whose pieces hold no valid block gives O = 0, LSE = -inf.
+template <int BT>
+__global__ void __launch_bounds__(BT * 2) attend_merge_kernel(AttendParams p) {
+  const GridGeom& g = p.g;
+  const int64_t tr = blockIdx.x;
+  const int64_t row = p.full_rows + tr;
+  const int t = threadIdx.x, qi = t >> 1, c0 = (t & 1) * 64;
+  const int qb = (int)(row % g.nqb);
+  const int64_t bh = row / g.nqb;
+  const int h = (int)(bh % g.heads);
+  const int b = (int)(bh / g.heads);
+  const int tq = qb / g.nbf, qpos = qb - tq * g.nbf;
+  const int qby = qpos / g.nbw, qbx = qpos - qby * g.nbw;
+  const int64_t qtok = block_token(g, tq, qby, qbx, qi);
+  const int64_t items = (p.rows - p.full_rows) * p.pieces;
+  const float* ml = p.part + items * BT * 128;
+
+  float m = -__builtin_huge_valf();
+  for (int pc = 0; pc < p.pieces; ++pc) m = fmaxf(m, ml[((tr * p.pieces + pc) * BT + qi) * 2]);
+  float acc[64];
+#pragma unroll
+  for (int c = 0; c < 64; ++c) acc[c] = 0.0f;
+  float l = 0.0f;
+  if (m > -__builtin_huge_valf()) {
+    for (int pc = 0; pc < p.pieces; ++pc) {
+      const int64_t it = tr * p.pieces + pc;
+      const float2 mlp = *reinterpret_cast<const float2*>(ml + (it * BT + qi) * 2);
+      const float w = __builtin_amdgcn_exp2f(mlp.x - m);   // 0 for an empty piece
+      l = fmaf(w, mlp.y, l);
+      const float4* src = reinterpret_cast<const float4*>(p.part + (it * BT + qi) * 128 + c0);
+#pragma unroll
+      for (int c4 = 0; c4 < 16; ++c4) {
+        const float4 x = src[c4];
+        acc[4 * c4 + 0] = fmaf(w, x.x, acc[4 * c4 + 0]);
+        acc[4 * c4 + 1] = fmaf(w, x.y, acc[4 * c4 + 1]);
+        acc[4 * c4 + 2] = fmaf(w, x.z, acc[4 * c4 + 2]);
+        acc[4 * c4 + 3] = fmaf(w, x.w, acc[4 * c4 + 3]);
+      }
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  uint16_t* orow = p.o + (int64_t)b * p.o_sb + qtok * p.o_ss + (int64_t)h * p.o_sh + c0;
+#pragma unroll
+  for (int c8 = 0; c8 < 8; ++c8) {
+    uint4 w;
+    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      f32x2_t x;
+      x[0] = acc[8 * c8 + 2 * k2] * inv;
+      x[1] = acc[8 * c8 + 2 * k2 + 1] * inv;
+      wp[k2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+    }
+    *reinterpret_cast<uint4*>(orow + 8 * c8) = w;
+  }
+  if (p.lse && c0 == 0) {
+    const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * 0.69314718055994531f : -__builtin_huge_valf();
+    p.lse[((int64_t)b * g.heads + h) * g.q_tokens + qtok] = lse;
+  }
+}
+
+template <int BT>
+hipError_t launch_bt(const AttendParams& p, hipStream_t stream) {
+  const int64_t split = p.rows - p.full_rows;
+  const int64_t groups = p.full_rows + split * p.pieces;
+  hipLaunchKernelGGL(attend_fwd_kernel<BT>, dim3((unsigned)groups), dim3(Tile<BT>::kThreads), 0,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 0) return e;
+  hipLaunchKernelGGL(attend_merge_kernel<BT>, dim3((unsigned)split), dim3(BT * 2), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendParams& p, int block_tokens, hipStream_t stream) {
   if (p.rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)p.rows);
-  if (block_tokens == 128)
-    hipLaunchKernelGGL(attend_fwd_kernel<128>, grid, dim3(Tile<128>::kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attend_fwd_kernel<64>, grid, dim3(Tile<64>::kThreads), 0, stream, p);
-  return hipGetLastError();
+  return block_tokens == 128 ? launch_bt<128>(p, stream) : launch_bt<64>(p, stream);
 }
 
 }  // namespace lcsa

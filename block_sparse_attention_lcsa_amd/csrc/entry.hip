@@ -38,6 +38,24 @@ lcsa_status check_device() {
   return known[dev] > 0 ? LCSA_OK : fail(LCSA_ERR_DEVICE, "device %d is not gfx950", dev);
 }
 
+// Compute units of the current device (cached per device).
+lcsa_status device_cus(int* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256)
+    return fail(LCSA_ERR_DEVICE, "no current HIP device");
+  static std::mutex mu;
+  static int cached[256] = {0};
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return fail(LCSA_ERR_DEVICE, "cannot query the compute-unit count of device %d", dev);
+    cached[dev] = n;
+  }
+  *out = cached[dev];
+  return LCSA_OK;
+}
+
 lcsa_status check_view(const char* name, const lcsa_tensor* t, int64_t tokens, int heads,
                        bool allow_null_data = false) {
   if (!t) return fail(LCSA_ERR_NULL, "%s: tensor descriptor is NULL", name);
@@ -152,7 +170,8 @@ lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
 lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
                         const lcsa_tensor* v, const int32_t* d_row_ptr,
                         const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
-                        float* d_lse, void* stream) {
+                        float* d_lse, void* d_workspace, size_t workspace_bytes,
+                        void* stream) {
   lcsa::clear_error();
   if (!plan) return fail(LCSA_ERR_NULL, "lcsa_attend: plan is NULL");
   const lcsa_plan_info& in = plan->info;
@@ -170,7 +189,37 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   const int64_t in_block = (static_cast<int64_t>(in.block_h - 1) * plan->desc.grid_w + in.block_w) * 2;
   if (in_block * k->stride_s >= INT32_MAX || in_block * v->stride_s >= INT32_MAX)
     return fail(LCSA_ERR_SHAPE, "lcsa_attend: token stride too large for one key block");
+  if (d_workspace && reinterpret_cast<uintptr_t>(d_workspace) % 256)
+    return fail(LCSA_ERR_ALIGN, "lcsa_attend: workspace not 256-byte aligned");
   if ((st = lcsa::check_device())) return st;
+
+  // Split the rows of a last, partly filled round of workgroups: with S
+  // workgroups resident at once, rows % S rows would otherwise run alone on
+  // a mostly idle device.  Each of them becomes `pieces` workgroups over
+  // consecutive parts of its CSR range (at most S pieces in all), merged by
+  // a second kernel.
+  int64_t full_rows = in.rows;
+  int pieces = 1;
+  if (d_workspace) {
+    int cus = 0;
+    if ((st = lcsa::device_cus(&cus))) return st;
+    const int64_t slots = static_cast<int64_t>(cus) * lcsa::attend_groups_per_cu(in.block_tokens);
+    const int64_t tail = in.rows % slots;
+    if (tail > 0) {
+      int64_t want = slots / tail;
+      const int64_t cap = in.max_row_nnz < 16 ? in.max_row_nnz : 16;
+      if (want > cap) want = cap;
+      if (want >= 2) {
+        const uint64_t need =
+            static_cast<uint64_t>(tail * want) * lcsa::attend_piece_bytes(in.block_tokens);
+        if (workspace_bytes < need)
+          return fail(LCSA_ERR_WORKSPACE, "lcsa_attend: workspace %zu bytes < %llu needed",
+                      workspace_bytes, (unsigned long long)need);
+        full_rows = in.rows - tail;
+        pieces = static_cast<int>(want);
+      }
+    }
+  }
 
   lcsa::AttendParams ap;
   ap.g = lcsa::make_geom(plan);
@@ -186,6 +235,9 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   ap.col_idx = d_col_idx;
   ap.nnz = nnz;
   ap.rows = in.rows;
+  ap.full_rows = full_rows;
+  ap.pieces = pieces;
+  ap.part = static_cast<float*>(d_workspace);
   ap.scale_log2 = static_cast<float>(in.scale * 1.4426950408889634);
   const hipError_t e = lcsa::launch_attend(ap, in.block_tokens, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "attend launch: %s", hipGetErrorString(e));

@@ -51,7 +51,13 @@ struct AttendParams {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int64_t nnz;
-  int64_t rows;          // CSR rows = workgroups
+  int64_t rows;          // CSR rows
+  // Rows [0, full_rows) run as one workgroup each; every later row is split
+  // into `pieces` parts of its CSR range, each a workgroup that writes its
+  // unnormalised partial result to `part` for the merge kernel.
+  int64_t full_rows;
+  int32_t pieces;
+  float* part;           // [items][BT][128] partial O, then [items][BT][2] (m, l)
   float scale_log2;      // softmax scale * log2(e)
 };
 

@@ -23,6 +23,9 @@ constexpr int kMaxWindow = 1024;
 // Query frames scored together by one select workgroup.
 constexpr int kSelectFrames = 6;
 constexpr int kHeadDim = 128;
+// Compute units of the largest gfx950 device (MI355X, MI350X); sizes the
+// attention workspace for split rows.
+constexpr uint64_t kMaxCus = 256;
 
 // Record a formatted error for lcsa_last_error() and return the status.
 lcsa_status fail(lcsa_status st, const char* fmt, ...);

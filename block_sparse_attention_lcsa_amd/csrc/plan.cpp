@@ -195,6 +195,10 @@ lcsa_status lcsa_plan_create(const lcsa_desc* d, lcsa_plan_t* out) {
   // (b, h) [B][H][128][NKB], both float64.
   in.select_workspace_bytes = static_cast<uint64_t>(d->batch) * d->heads * 128ull *
                               static_cast<uint64_t>(nqb + nkb) * 8ull;
+  // Attend: at most one partly filled round of split pieces, i.e. as many
+  // pieces as workgroups fit on the largest gfx950 device at once.
+  const uint64_t bt = static_cast<uint64_t>(in.block_tokens);
+  in.attend_workspace_bytes = lcsa::kMaxCus * (8 / (bt / 32)) * bt * (128 + 2) * 4;
 
   try {
     p->row_ptr.resize(static_cast<size_t>(rows) + 1);

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LCSA_ABI_VERSION 1
+#define LCSA_ABI_VERSION 2
 
 typedef int32_t lcsa_status;
 #define LCSA_OK 0
@@ -129,6 +129,7 @@ typedef struct lcsa_plan_info {
   int64_t q_tokens;
   int64_t kv_tokens;
   uint64_t select_workspace_bytes;
+  uint64_t attend_workspace_bytes; /* enough for any gfx950 device */
   double scale;                /* softmax scale actually used */
   double useful_flops;         /* 4 * head_dim * block_tokens^2 * nnz */
 } lcsa_plan_info;
@@ -180,7 +181,11 @@ lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
 /* Block-sparse attention forward: for each CSR row (b, h, query block) and
  * every token of every key block in the row, z = scale * q.k; online softmax
  * over those tokens; O = sum softmax(z) v, rounded to bf16 (nearest even);
- * LSE = max z + ln(sum exp(z - max z)) in float32.
+ * LSE = max z + ln(sum exp(z - max z)) in float32.  The attention step of
+ * LCSA: attention limited to the selected local blocks (agentlens FlashVSR
+ * summary, "How it works", item 2) run as a block-sparse kernel over a CSR
+ * block list (FlashVSR Hopper PR page, "Rebuild sparse attention for
+ * Hopper").
  *  q, k, v, o      device views; o is written, the others are read.
  *  d_row_ptr       device int32[rows + 1]; d_col_idx device int32[nnz].
  *                  Any CSR is accepted: row bounds are clamped to [0, nnz]
@@ -189,11 +194,19 @@ lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
  *                  A row with no valid block yields O = 0 and LSE = -inf.
  *  nnz             number of int32 in d_col_idx.
  *  d_lse           NULL, or device float[batch * heads * q_tokens].
- * Errors: NULL, ALIGN, INVALID (nnz < 0), DEVICE, LAUNCH. */
+ *  d_workspace     NULL, or a device buffer of workspace_bytes (256-byte
+ *                  aligned, at least attend_workspace_bytes) for partial
+ *                  results.  With it, the rows that would run in a last,
+ *                  partly filled round of workgroups are split into pieces
+ *                  over their block lists and merged by a second kernel;
+ *                  without it, every row is one workgroup.  Results agree
+ *                  to rounding; the contents are scratch.
+ * Errors: NULL, ALIGN, INVALID (nnz < 0), SHAPE, WORKSPACE, DEVICE, LAUNCH. */
 lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
                         const lcsa_tensor* v, const int32_t* d_row_ptr,
                         const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
-                        float* d_lse, void* stream);
+                        float* d_lse, void* d_workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Static text for a status code. */
 const char* lcsa_status_string(lcsa_status status);

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lcsa.abi_version() == 1
+    assert lcsa.abi_version() == 2
     lib = ctypes.CDLL(lcsa.lib_path())
     lib.lcsa_status_string.restype = ctypes.c_char_p
     texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
@@ -72,6 +72,9 @@ def test_plan_matches_oracle_geometry(name):
     assert inf["rows"] == len(rp) - 1 and inf["nnz"] == rp[-1]
     assert np.array_equal(p.row_ptr(), rp)
     assert inf["useful_flops"] == oracle.useful_flops(g, rp)
+    # room for one device-wide round of split pieces: 256 CUs x 8 waves
+    bt = g.block_tokens
+    assert inf["attend_workspace_bytes"] == 256 * (8 // (bt // 32)) * bt * (128 + 2) * 4
     for qb in range(0, g.nqb, max(1, g.nqb // 37)):
         assert np.array_equal(p.window(qb), oracle.window(g, qb))
 
@@ -138,10 +141,10 @@ def _select(p, q, k, rp=0x20000, ci=0x30000, ws=0x40000, ws_bytes=None):
     return lib.lcsa_select(p.handle, ctypes.byref(q), ctypes.byref(k), rp, ci, None, ws, wsb, None)
 
 
-def _attend(p, q, k, v, o, nnz=8):
+def _attend(p, q, k, v, o, nnz=8, ws=None, ws_bytes=0):
     lib = lcsa._lib
     return lib.lcsa_attend(p.handle, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
-                           0x20000, 0x30000, nnz, ctypes.byref(o), None, None)
+                           0x20000, 0x30000, nnz, ctypes.byref(o), None, ws, ws_bytes, None)
 
 
 def test_entry_point_validation_statuses():
@@ -159,6 +162,7 @@ def test_entry_point_validation_statuses():
     assert _select(p, bad_dtype, good) == 2                           # INVALID dtype
     assert _attend(p, good, good, good, good, nnz=-1) == 2            # INVALID nnz
     assert _attend(p, good, good, _fake_view(addr=0x10004), good) == 4
+    assert _attend(p, good, good, good, good, ws=0x40040, ws_bytes=1 << 20) == 4  # ALIGN workspace
     assert lcsa._lib.lcsa_select(None, None, None, None, None, None, None, 0, None) == 1
     big = lcsa.Plan.from_desc(dict(li.CONFIGS["first_2048x3840"], local_range=15))
     assert big.info["max_window"] > 1024
