@@ -16,6 +16,7 @@ cpu_baseline = the float64 CPU oracle on a bounded sample of the same
 workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --workload stream_768x1280 --ring   # streaming steady state
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -117,6 +118,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ring", action="store_true",
+                    help="K/V in a frame ring with the pooled-K cache: each step pools only "
+                         "the chunk's q_frames new frames (streaming steady state)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -150,14 +154,37 @@ def main():
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
 
+    new_frames = info["kv_frames"]
+    if args.ring:
+        # ring of kv_frames slots, window frame t in slot (t + 1) % slots;
+        # the cache is filled once, then each step pools the newest q_frames
+        kvf, ft = info["kv_frames"], desc["grid_h"] * desc["grid_w"]
+        slots = kvf
+        frame_slot = [(t + 1) % slots for t in range(kvf)]
+        ring = lcsa.kv_ring(slots, frame_slot)
+        k_ring, v_ring = torch.empty_like(k), torch.empty_like(v)
+        for t in range(kvf):
+            sl = frame_slot[t]
+            k_ring[:, sl * ft:(sl + 1) * ft] = k[:, t * ft:(t + 1) * ft]
+            v_ring[:, sl * ft:(sl + 1) * ft] = v[:, t * ft:(t + 1) * ft]
+        kcache = torch.empty(lcsa.kcache_bytes(plan, slots) // 8, dtype=torch.float64, device=dev)
+        lcsa.select_ring(plan, q, k_ring, ring, kvf, kcache, workspace=ws)
+        new_frames = min(desc["q_frames"], kvf)
+
     def step(ev=None):
         p = lcsa.Plan.from_desc(desc)                      # host plan (per shape)
         if ev:
             ev[0].record(stream)
-        rp, ci = lcsa.select(p, q, k, workspace=ws)
+        if args.ring:
+            rp, ci = lcsa.select_ring(p, q, k_ring, ring, new_frames, kcache, workspace=ws)
+        else:
+            rp, ci = lcsa.select(p, q, k, workspace=ws)
         if ev:
             ev[1].record(stream)
-        lcsa.attend(p, q, k, v, rp, ci, out=out, workspace=att_ws)
+        if args.ring:
+            lcsa.attend_ring(p, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
+        else:
+            lcsa.attend(p, q, k, v, rp, ci, out=out, workspace=att_ws)
         if ev:
             ev[2].record(stream)
 
@@ -186,7 +213,8 @@ def main():
     achieved = flops / (att_avg * 1e-3) / 1e12
     # select: algorithmic HBM bytes = Q and K read once (bf16) + the CSR
     # written (row_ptr and col_idx, int32)
-    sel_bytes = (2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + info["kv_tokens"])
+    pooled_kv_tokens = info["kv_tokens"] * new_frames // info["kv_frames"]
+    sel_bytes = (2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + pooled_kv_tokens)
                  + 4 * (info["rows"] + 1 + info["nnz"]))
     sel_gbs = sel_bytes / (sel_avg * 1e-3) / 1e9
 
@@ -210,6 +238,8 @@ def main():
             "block": [info["block_h"], info["block_w"]], "local_range": desc["local_range"],
             "k": info["k"], "selected_pairs": info["nnz"], "useful_tflop": flops / 1e12,
             "seed": args.seed, "inputs_sha256": inp.sha256,
+            "kv_storage": "frame ring + pooled-K cache" if args.ring else "contiguous window",
+            "pooled_kv_frames": new_frames,
         },
         "select_ms": sel_avg,
         "attend_ms": att_avg,

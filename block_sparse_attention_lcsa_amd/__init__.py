@@ -18,7 +18,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "LcsaError", "select", "attend", "lib_path", "abi_version", "EXPORTS"]
+__all__ = ["Plan", "LcsaError", "select", "attend", "select_ring", "attend_ring", "lib_path",
+           "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -37,9 +38,10 @@ _lib = ctypes.CDLL(lib_path())
 # Every symbol include/lcsa.h declares.
 EXPORTS = [
     "lcsa_plan_create", "lcsa_plan_destroy", "lcsa_plan_get_info", "lcsa_plan_row_ptr",
-    "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_status_string",
-    "lcsa_last_error", "lcsa_abi_version",
+    "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_select_ring", "lcsa_attend_ring",
+    "lcsa_status_string", "lcsa_last_error", "lcsa_abi_version",
 ]
+MAX_KV_FRAMES = 64
 
 LCSA_DTYPE_BF16 = 1
 STATUS = {0: "LCSA_OK", 1: "LCSA_ERR_NULL", 2: "LCSA_ERR_INVALID", 3: "LCSA_ERR_SHAPE",
@@ -64,6 +66,10 @@ class LcsaTensor(ctypes.Structure):
                 ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
 
+class LcsaKvRing(ctypes.Structure):
+    _fields_ = [("slots", ctypes.c_int32), ("frame_slot", ctypes.c_int32 * 64)]
+
+
 class LcsaPlanInfo(ctypes.Structure):
     _fields_ = [("kv_frames", ctypes.c_int32), ("blocks_per_frame", ctypes.c_int32),
                 ("nbh", ctypes.c_int32), ("nbw", ctypes.c_int32), ("nqb", ctypes.c_int32),
@@ -74,7 +80,8 @@ class LcsaPlanInfo(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("nnz", ctypes.c_int64),
                 ("q_tokens", ctypes.c_int64), ("kv_tokens", ctypes.c_int64),
                 ("select_workspace_bytes", ctypes.c_uint64),
-                ("attend_workspace_bytes", ctypes.c_uint64), ("scale", ctypes.c_double),
+                ("attend_workspace_bytes", ctypes.c_uint64),
+                ("kcache_slot_bytes", ctypes.c_uint64), ("scale", ctypes.c_double),
                 ("useful_flops", ctypes.c_double)]
 
 
@@ -97,6 +104,15 @@ _lib.lcsa_attend.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(Lcsa
                              ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_int64,
                              ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_size_t, _P]
 _lib.lcsa_attend.restype = ctypes.c_int32
+_lib.lcsa_select_ring.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                  ctypes.POINTER(LcsaKvRing), ctypes.c_int32, _P,
+                                  _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lcsa_select_ring.restype = ctypes.c_int32
+_lib.lcsa_attend_ring.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                  ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaKvRing), _P, _P,
+                                  ctypes.c_int64, ctypes.POINTER(LcsaTensor), _P, _P,
+                                  ctypes.c_size_t, _P]
+_lib.lcsa_attend_ring.restype = ctypes.c_int32
 _lib.lcsa_status_string.argtypes = [ctypes.c_int32]
 _lib.lcsa_status_string.restype = ctypes.c_char_p
 _lib.lcsa_last_error.argtypes = []
@@ -271,6 +287,109 @@ def attend(plan: Plan, q, k, v, row_ptr, col_idx, out=None, return_lse: bool = F
                           lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
                           _stream_ptr(q, stream))
     _check(st, "lcsa_attend")
+    if return_lse:
+        return out, lse
+    return out
+
+
+def kv_ring(slots: int, frame_slot) -> LcsaKvRing:
+    """Frame-ring descriptor: window frame t (oldest first) lives in ring slot
+    frame_slot[t] of K/V ring buffers that hold `slots` frames."""
+    r = LcsaKvRing()
+    r.slots = int(slots)
+    fs = [int(x) for x in frame_slot]
+    if len(fs) > MAX_KV_FRAMES:
+        raise ValueError(f"at most {MAX_KV_FRAMES} window frames")
+    for i, x in enumerate(fs):
+        r.frame_slot[i] = x
+    return r
+
+
+def _check_ring_tensor(t, plan: Plan, slots: int, name: str):
+    d = plan.desc
+    want = (d["batch"], slots * d["grid_h"] * d["grid_w"], d["heads"], d["head_dim"])
+    if tuple(t.shape) != want:
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {want}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def kcache_bytes(plan: Plan, slots: int) -> int:
+    """Bytes of the pooled-K cache of a ring with `slots` frames."""
+    return int(plan.info["kcache_slot_bytes"]) * int(slots)
+
+
+def select_ring(plan: Plan, q, k_ring, ring: LcsaKvRing, new_frames: int, kcache,
+                return_scores: bool = False, workspace=None, stream=None):
+    """Top-k block selection with K read from a frame ring and the pooled K of
+    older frames taken from `kcache` (float64 device tensor of
+    kcache_bytes(plan, ring.slots) bytes); the newest `new_frames` window
+    frames are pooled and stored there."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_ring_tensor(k_ring, plan, ring.slots, "k_ring")
+    if kcache.dtype != torch.float64 or kcache.numel() * 8 < kcache_bytes(plan, ring.slots):
+        raise ValueError("kcache must be float64 with kcache_bytes(plan, slots) bytes")
+    inf = plan.info
+    dev = q.device
+    row_ptr = torch.empty(inf["rows"] + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(inf["nnz"], 1), dtype=torch.int32, device=dev)[: inf["nnz"]]
+    if workspace is None:
+        workspace = torch.empty(max(int(inf["select_workspace_bytes"]), 256), dtype=torch.uint8,
+                                device=dev)
+    scores = None
+    if return_scores:
+        d = plan.desc
+        scores = torch.empty((d["batch"], d["heads"], inf["nqb"], inf["nkb"]),
+                             dtype=torch.float64, device=dev)
+    qv, kv = tensor_view(q), tensor_view(k_ring)
+    st = _lib.lcsa_select_ring(plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(ring),
+                               int(new_frames), kcache.data_ptr(), row_ptr.data_ptr(),
+                               col_idx.data_ptr() if inf["nnz"] else None,
+                               scores.data_ptr() if scores is not None else None,
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream_ptr(q, stream))
+    _check(st, "lcsa_select_ring")
+    if return_scores:
+        return row_ptr, col_idx, scores
+    return row_ptr, col_idx
+
+
+def attend_ring(plan: Plan, q, k_ring, v_ring, ring: LcsaKvRing, row_ptr, col_idx, out=None,
+                return_lse: bool = False, workspace=None, split_tail: bool = True, stream=None):
+    """Block-sparse attention with K and V read from a frame ring."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_ring_tensor(k_ring, plan, ring.slots, "k_ring")
+    _check_ring_tensor(v_ring, plan, ring.slots, "v_ring")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != plan.info["rows"] + 1 or not row_ptr.is_contiguous():
+        raise ValueError("row_ptr must hold rows + 1 contiguous int32")
+    if not col_idx.is_contiguous():
+        raise ValueError("col_idx must be contiguous")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    else:
+        _check_shape(out, plan, "q_tokens", "out")
+    lse = None
+    if return_lse:
+        d = plan.desc
+        lse = torch.empty((d["batch"], d["heads"], plan.info["q_tokens"]), dtype=torch.float32,
+                          device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if split_tail:
+        if workspace is None:
+            workspace = torch.empty(int(plan.info["attend_workspace_bytes"]), dtype=torch.uint8,
+                                    device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    qv, kv, vv, ov = tensor_view(q), tensor_view(k_ring), tensor_view(v_ring), tensor_view(out)
+    st = _lib.lcsa_attend_ring(plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
+                               ctypes.byref(ring), row_ptr.data_ptr(),
+                               col_idx.data_ptr() if col_idx.numel() else None, col_idx.numel(),
+                               ctypes.byref(ov), lse.data_ptr() if lse is not None else None,
+                               ws_ptr, ws_bytes, _stream_ptr(q, stream))
+    _check(st, "lcsa_attend_ring")
     if return_lse:
         return out, lse
     return out

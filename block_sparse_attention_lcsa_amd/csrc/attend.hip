@@ -221,7 +221,8 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   auto block_offset = [&](int kb, int64_t ss2) {
     const int t = fast_div(kb, g.nbf_m, g.nbf_s), ps = kb - t * g.nbf;
     const int kby = fast_div(ps, g.nbw_m, g.nbw_s), kbx = ps - kby * g.nbw;
-    const int64_t tok0 = ((int64_t)t * g.grid_h + (int64_t)kby * g.block_h) * g.grid_w + (int64_t)kbx * g.block_w;
+    const int64_t tok0 = ((int64_t)g.kv_slot[t] * g.grid_h + (int64_t)kby * g.block_h) * g.grid_w +
+                         (int64_t)kbx * g.block_w;
     return tok0 * ss2;
   };
   const uint32_t k_lds_addr = lds_address(k_lds) + wave * 1024;

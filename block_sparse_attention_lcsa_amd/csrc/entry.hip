@@ -82,7 +82,7 @@ void magic_div(uint32_t d, uint32_t* m, uint32_t* shift) {
   *shift = 31 + l;
 }
 
-GridGeom make_geom(const lcsa_plan_s* p) {
+GridGeom make_geom(const lcsa_plan_s* p, const lcsa_kv_ring* ring) {
   const lcsa_plan_info& in = p->info;
   GridGeom g;
   g.heads = p->desc.heads;
@@ -104,7 +104,19 @@ GridGeom make_geom(const lcsa_plan_s* p) {
   g.q_tokens = in.q_tokens;
   magic_div(static_cast<uint32_t>(g.nbf), &g.nbf_m, &g.nbf_s);
   magic_div(static_cast<uint32_t>(g.nbw), &g.nbw_m, &g.nbw_s);
+  for (int t = 0; t < kMaxKvFrames; ++t)
+    g.kv_slot[t] = t < g.kv_frames ? (ring ? ring->frame_slot[t] : t) : 0;
   return g;
+}
+
+lcsa_status check_ring(const char* fn, const lcsa_plan_s* p, const lcsa_kv_ring* ring) {
+  if (!ring) return fail(LCSA_ERR_NULL, "%s: ring is NULL", fn);
+  if (ring->slots < 1) return fail(LCSA_ERR_INVALID, "%s: ring has %d slots", fn, ring->slots);
+  for (int t = 0; t < p->info.kv_frames; ++t)
+    if (ring->frame_slot[t] < 0 || ring->frame_slot[t] >= ring->slots)
+      return fail(LCSA_ERR_INVALID, "%s: frame %d is in slot %d, outside [0, %d)", fn, t,
+                  ring->frame_slot[t], ring->slots);
+  return LCSA_OK;
 }
 
 View make_view(const lcsa_tensor* t) {
@@ -117,81 +129,83 @@ View make_view(const lcsa_tensor* t) {
 }
 
 }  // namespace
-}  // namespace lcsa
 
-using lcsa::fail;
-
-extern "C" {
-
-lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
-                        int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
-                        void* d_workspace, size_t workspace_bytes, void* stream) {
-  lcsa::clear_error();
-  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_select: plan is NULL");
+// Shared body of lcsa_select (ring == NULL: K is the contiguous window, the
+// pooled K of every window frame goes to the workspace) and lcsa_select_ring
+// (the newest new_frames frames are pooled into the caller's cache).
+lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tensor* q,
+                        const lcsa_tensor* k, const lcsa_kv_ring* ring, int new_frames,
+                        double* d_kcache, int32_t* d_row_ptr, int32_t* d_col_idx,
+                        double* d_scores, void* d_workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
-  if ((st = lcsa::check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
-  if ((st = lcsa::check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
-  if (!d_row_ptr || !d_col_idx) return fail(LCSA_ERR_NULL, "lcsa_select: CSR buffers are NULL");
-  if (in.max_window > lcsa::kMaxWindow)
+  if ((st = check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
+  if ((st = check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
+  if (!d_row_ptr || !d_col_idx) return fail(LCSA_ERR_NULL, "%s: CSR buffers are NULL", fn);
+  if (in.max_window > kMaxWindow)
     return fail(LCSA_ERR_SHAPE, "window of %d key blocks exceeds the select limit of %d",
-                in.max_window, lcsa::kMaxWindow);
-  if (!d_workspace || workspace_bytes < in.select_workspace_bytes)
-    return fail(LCSA_ERR_WORKSPACE, "select needs %llu workspace bytes, got %llu",
-                (unsigned long long)in.select_workspace_bytes,
-                (unsigned long long)workspace_bytes);
+                in.max_window, kMaxWindow);
+  const size_t qbar_bytes = static_cast<size_t>(in.rows) * 128 * sizeof(double);
+  const uint64_t ws_need = ring ? qbar_bytes : in.select_workspace_bytes;
+  if (!d_workspace || workspace_bytes < ws_need)
+    return fail(LCSA_ERR_WORKSPACE, "%s needs %llu workspace bytes, got %llu", fn,
+                (unsigned long long)ws_need, (unsigned long long)workspace_bytes);
   if (reinterpret_cast<uintptr_t>(d_workspace) % 256)
     return fail(LCSA_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if ((st = lcsa::check_device())) return st;
+  if ((st = check_device())) return st;
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t qbar_bytes = static_cast<size_t>(in.rows) * 128 * sizeof(double);
-  lcsa::PoolParams pp;
-  pp.g = lcsa::make_geom(plan);
-  pp.q = lcsa::make_view(q);
-  pp.k = lcsa::make_view(k);
+  PoolParams pp;
+  pp.g = make_geom(plan, ring);
+  pp.q = make_view(q);
+  pp.k = make_view(k);
   pp.qbar = static_cast<double*>(d_workspace);
-  pp.kbar_t = reinterpret_cast<double*>(static_cast<char*>(d_workspace) + qbar_bytes);
-  hipError_t e = lcsa::launch_pool(pp, plan->desc.batch, in.block_tokens, s);
+  pp.kcache = ring ? d_kcache
+                   : reinterpret_cast<double*>(static_cast<char*>(d_workspace) + qbar_bytes);
+  pp.k_first = ring ? in.kv_frames - new_frames : 0;
+  hipError_t e = launch_pool(pp, plan->desc.batch, in.block_tokens, s);
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "pool launch: %s", hipGetErrorString(e));
 
-  lcsa::SelectParams sp;
+  SelectParams sp;
   sp.g = pp.g;
   sp.qbar = pp.qbar;
-  sp.kbar_t = pp.kbar_t;
+  sp.kcache = pp.kcache;
+  sp.batch = plan->desc.batch;
   sp.row_ptr = d_row_ptr;
   sp.col_idx = d_col_idx;
   sp.scores = d_scores;
-  e = lcsa::launch_select(sp, plan->desc.batch, in.max_window, s);
+  e = launch_select(sp, plan->desc.batch, in.max_window, s);
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "select launch: %s", hipGetErrorString(e));
   return LCSA_OK;
 }
 
-lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
-                        const lcsa_tensor* v, const int32_t* d_row_ptr,
-                        const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
-                        float* d_lse, void* d_workspace, size_t workspace_bytes,
-                        void* stream) {
-  lcsa::clear_error();
-  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_attend: plan is NULL");
+// Shared body of lcsa_attend (ring == NULL) and lcsa_attend_ring.
+lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tensor* q,
+                        const lcsa_tensor* k, const lcsa_tensor* v, const lcsa_kv_ring* ring,
+                        const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
+                        const lcsa_tensor* o, float* d_lse, void* d_workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
-  if ((st = lcsa::check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
-  if ((st = lcsa::check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
-  if ((st = lcsa::check_view("v", v, in.kv_tokens, plan->desc.heads))) return st;
-  if ((st = lcsa::check_view("o", o, in.q_tokens, plan->desc.heads))) return st;
-  if (!d_row_ptr) return fail(LCSA_ERR_NULL, "lcsa_attend: row_ptr is NULL");
-  if (nnz < 0) return fail(LCSA_ERR_INVALID, "lcsa_attend: nnz %lld < 0", (long long)nnz);
-  if (nnz > 0 && !d_col_idx) return fail(LCSA_ERR_NULL, "lcsa_attend: col_idx is NULL");
+  if ((st = check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
+  if ((st = check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
+  if ((st = check_view("v", v, in.kv_tokens, plan->desc.heads))) return st;
+  if ((st = check_view("o", o, in.q_tokens, plan->desc.heads))) return st;
+  if (!d_row_ptr) return fail(LCSA_ERR_NULL, "%s: row_ptr is NULL", fn);
+  if (nnz < 0) return fail(LCSA_ERR_INVALID, "%s: nnz %lld < 0", fn, (long long)nnz);
+  if (nnz > 0 && !d_col_idx) return fail(LCSA_ERR_NULL, "%s: col_idx is NULL", fn);
   if (nnz >= INT32_MAX)
-    return fail(LCSA_ERR_SHAPE, "lcsa_attend: nnz %lld exceeds int32 CSR", (long long)nnz);
+    return fail(LCSA_ERR_SHAPE, "%s: nnz %lld exceeds int32 CSR", fn, (long long)nnz);
   // The kernel addresses K/V rows inside one block with 32-bit byte offsets.
   const int64_t in_block = (static_cast<int64_t>(in.block_h - 1) * plan->desc.grid_w + in.block_w) * 2;
   if (in_block * k->stride_s >= INT32_MAX || in_block * v->stride_s >= INT32_MAX)
-    return fail(LCSA_ERR_SHAPE, "lcsa_attend: token stride too large for one key block");
+    return fail(LCSA_ERR_SHAPE, "%s: token stride too large for one key block", fn);
   if (d_workspace && reinterpret_cast<uintptr_t>(d_workspace) % 256)
-    return fail(LCSA_ERR_ALIGN, "lcsa_attend: workspace not 256-byte aligned");
-  if ((st = lcsa::check_device())) return st;
+    return fail(LCSA_ERR_ALIGN, "%s: workspace not 256-byte aligned", fn);
+  if ((st = check_device())) return st;
 
   // Split the rows of a last, partly filled round of workgroups: with S
   // workgroups resident at once, rows % S rows would otherwise run alone on
@@ -202,8 +216,8 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   int pieces = 1;
   if (d_workspace) {
     int cus = 0;
-    if ((st = lcsa::device_cus(&cus))) return st;
-    const int64_t slots = static_cast<int64_t>(cus) * lcsa::attend_groups_per_cu(in.block_tokens);
+    if ((st = device_cus(&cus))) return st;
+    const int64_t slots = static_cast<int64_t>(cus) * attend_groups_per_cu(in.block_tokens);
     const int64_t tail = in.rows % slots;
     if (tail > 0) {
       int64_t want = slots / tail;
@@ -211,9 +225,9 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
       if (want > cap) want = cap;
       if (want >= 2) {
         const uint64_t need =
-            static_cast<uint64_t>(tail * want) * lcsa::attend_piece_bytes(in.block_tokens);
+            static_cast<uint64_t>(tail * want) * attend_piece_bytes(in.block_tokens);
         if (workspace_bytes < need)
-          return fail(LCSA_ERR_WORKSPACE, "lcsa_attend: workspace %zu bytes < %llu needed",
+          return fail(LCSA_ERR_WORKSPACE, "%s: workspace %zu bytes < %llu needed", fn,
                       workspace_bytes, (unsigned long long)need);
         full_rows = in.rows - tail;
         pieces = static_cast<int>(want);
@@ -221,11 +235,11 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
     }
   }
 
-  lcsa::AttendParams ap;
-  ap.g = lcsa::make_geom(plan);
-  ap.q = lcsa::make_view(q);
-  ap.k = lcsa::make_view(k);
-  ap.v = lcsa::make_view(v);
+  AttendParams ap;
+  ap.g = make_geom(plan, ring);
+  ap.q = make_view(q);
+  ap.k = make_view(k);
+  ap.v = make_view(v);
   ap.o = static_cast<uint16_t*>(o->data);
   ap.o_sb = o->stride_b;
   ap.o_ss = o->stride_s;
@@ -239,9 +253,64 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   ap.pieces = pieces;
   ap.part = static_cast<float*>(d_workspace);
   ap.scale_log2 = static_cast<float>(in.scale * 1.4426950408889634);
-  const hipError_t e = lcsa::launch_attend(ap, in.block_tokens, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_attend(ap, in.block_tokens, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "attend launch: %s", hipGetErrorString(e));
   return LCSA_OK;
+}
+
+}  // namespace lcsa
+
+using lcsa::fail;
+
+extern "C" {
+
+lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                        int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                        void* d_workspace, size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  return lcsa::select_impl("lcsa_select", plan, q, k, nullptr, 0, nullptr, d_row_ptr, d_col_idx,
+                           d_scores, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_select_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,
+                             const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
+                             int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                             void* d_workspace, size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_select_ring: plan is NULL");
+  lcsa_status st;
+  if ((st = lcsa::check_ring("lcsa_select_ring", plan, ring))) return st;
+  if (new_frames < 0 || new_frames > plan->info.kv_frames)
+    return fail(LCSA_ERR_INVALID, "lcsa_select_ring: new_frames %d outside [0, %d]", new_frames,
+                plan->info.kv_frames);
+  if (!d_kcache) return fail(LCSA_ERR_NULL, "lcsa_select_ring: pooled-K cache is NULL");
+  if (reinterpret_cast<uintptr_t>(d_kcache) % 256)
+    return fail(LCSA_ERR_ALIGN, "lcsa_select_ring: pooled-K cache not 256-byte aligned");
+  return lcsa::select_impl("lcsa_select_ring", plan, q, k_ring, ring, new_frames, d_kcache,
+                           d_row_ptr, d_col_idx, d_scores, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                        const lcsa_tensor* v, const int32_t* d_row_ptr,
+                        const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
+                        float* d_lse, void* d_workspace, size_t workspace_bytes,
+                        void* stream) {
+  lcsa::clear_error();
+  return lcsa::attend_impl("lcsa_attend", plan, q, k, v, nullptr, d_row_ptr, d_col_idx, nnz, o,
+                           d_lse, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_attend_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,
+                             const lcsa_tensor* v_ring, const lcsa_kv_ring* ring,
+                             const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
+                             const lcsa_tensor* o, float* d_lse, void* d_workspace,
+                             size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_attend_ring: plan is NULL");
+  lcsa_status st;
+  if ((st = lcsa::check_ring("lcsa_attend_ring", plan, ring))) return st;
+  return lcsa::attend_impl("lcsa_attend_ring", plan, q, k_ring, v_ring, ring, d_row_ptr,
+                           d_col_idx, nnz, o, d_lse, d_workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 
 namespace lcsa {
 
+constexpr int kMaxKvFrames = 64;
+
 // Geometry of the token grid and its blocks, shared by every kernel.
 struct GridGeom {
   int32_t heads;
@@ -19,6 +21,9 @@ struct GridGeom {
   // Division by nbf and nbw as a multiply and shift (exact for n < 2^31):
   // n / d == (n * m) >> s with a 64-bit product.
   uint32_t nbf_m, nbf_s, nbw_m, nbw_s;
+  // Frame of the K/V storage holding KV-window frame t (the identity for a
+  // contiguous window, ring slots otherwise).
+  int32_t kv_slot[kMaxKvFrames];
 };
 
 struct View {
@@ -26,17 +31,20 @@ struct View {
   int64_t sb, ss, sh;    // strides in elements
 };
 
+// Pooled K lives per storage frame: kcache[slot][B*H][128][NBF].
 struct PoolParams {
   GridGeom g;
   View q, k;
   double* qbar;          // [B][H][NQB][128]
-  double* kbar_t;        // [B][H][128][NKB]
+  double* kcache;        // [slots][B*H][128][NBF]
+  int32_t k_first;       // first KV-window frame whose K blocks are pooled
 };
 
 struct SelectParams {
   GridGeom g;
   const double* qbar;    // [B][H][NQB][128]
-  const double* kbar_t;  // [B][H][128][NKB]
+  const double* kcache;  // [slots][B*H][128][NBF]
+  int32_t batch;
   int32_t* row_ptr;
   int32_t* col_idx;
   double* scores;        // optional [B][H][NQB][NKB]

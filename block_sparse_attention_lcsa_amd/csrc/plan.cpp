@@ -129,6 +129,10 @@ lcsa_status lcsa_plan_create(const lcsa_desc* d, lcsa_plan_t* out) {
   if (nkb > INT32_MAX / 2 || rows >= INT32_MAX || fs * kvf > INT32_MAX)
     return fail(LCSA_ERR_SHAPE, "problem too large for 32-bit block and token indices");
 
+  if (kvf > LCSA_MAX_KV_FRAMES)
+    return fail(LCSA_ERR_SHAPE, "KV window of %lld frames exceeds %d", (long long)kvf,
+                LCSA_MAX_KV_FRAMES);
+
   int64_t k;
   if (d->topk > 0) {
     k = d->topk;
@@ -199,6 +203,8 @@ lcsa_status lcsa_plan_create(const lcsa_desc* d, lcsa_plan_t* out) {
   // pieces as workgroups fit on the largest gfx950 device at once.
   const uint64_t bt = static_cast<uint64_t>(in.block_tokens);
   in.attend_workspace_bytes = lcsa::kMaxCus * (8 / (bt / 32)) * bt * (128 + 2) * 4;
+  in.kcache_slot_bytes = static_cast<uint64_t>(d->batch) * d->heads * 128ull *
+                         static_cast<uint64_t>(nbf) * 8ull;
 
   try {
     p->row_ptr.resize(static_cast<size_t>(rows) + 1);

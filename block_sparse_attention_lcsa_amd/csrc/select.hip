@@ -48,18 +48,21 @@ __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, 
   return ((int64_t)t * g.grid_h + y) * g.grid_w + x;
 }
 
-// grid (NQB + NKB, heads, batch): x < NQB pools query block x, otherwise key
-// block x - NQB.  Thread (c, tg) sums channels 8c..8c+7 of tokens tg, tg+16..
+// grid (NQB + pooled key blocks, heads, batch): x < NQB pools query block x,
+// otherwise key block x - NQB of the KV-window frames k_first onwards, read
+// from (and stored for) their storage frame kv_slot[t].  Thread (c, tg) sums
+// channels 8c..8c+7 of tokens tg, tg+16, ...
 template <int BT>
 __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
   __shared__ double red[16 * 128];
   const GridGeom& g = p.g;
   const int h = blockIdx.y, b = blockIdx.z;
   const bool is_q = (int)blockIdx.x < g.nqb;
-  const int blk = is_q ? (int)blockIdx.x : (int)blockIdx.x - g.nqb;
+  const int blk = is_q ? (int)blockIdx.x : (int)blockIdx.x - g.nqb + p.k_first * g.nbf;
   const View& x = is_q ? p.q : p.k;
   const int t = blk / g.nbf, pos = blk - t * g.nbf;
   const int by = pos / g.nbw, bx = pos - by * g.nbw;
+  const int tf = is_q ? t : g.kv_slot[t];   // frame of the storage
   const uint16_t* base = x.data + (int64_t)b * x.sb + (int64_t)h * x.sh;
   const int tid = threadIdx.x, c = tid & 15, tg = tid >> 4;
   double acc[8];
@@ -68,7 +71,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
 #pragma unroll
   for (int i = 0; i < BT / 16; ++i) {
     const int j = tg + 16 * i;
-    const uint4 w = *reinterpret_cast<const uint4*>(base + block_token(g, t, by, bx, j) * x.ss + c * 8);
+    const uint4 w = *reinterpret_cast<const uint4*>(base + block_token(g, tf, by, bx, j) * x.ss + c * 8);
     acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
     acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
     acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
@@ -86,7 +89,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
     if (is_q)
       p.qbar[(bh * g.nqb + blk) * 128 + tid] = s;
     else
-      p.kbar_t[(bh * 128 + tid) * g.nkb + blk] = s;
+      p.kcache[(((int64_t)tf * gridDim.z * g.heads + bh) * 128 + tid) * g.nbf + pos] = s;
   }
 }
 
@@ -143,24 +146,28 @@ __device__ void select_row(const SelectParams& p, const WindowBox& w, int b, int
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-  // Lane-per-candidate float64 scores: candidate e = lane + 64 j.
+  // Lane-per-candidate float64 scores: candidate e = lane + 64 j.  Pooled K
+  // of key block (t, pos) sits at kcache[kv_slot[t]][bh][d][pos].
   int kb[M];
+  int64_t koff[M];
   bool valid[M];
   double acc[M];
-  const double* kcol = p.kbar_t + bh * 128 * g.nkb;
+  const int64_t bh_all = (int64_t)p.batch * g.heads;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const int e = lane + 64 * j;
     valid[j] = e < w.n;
     kb[j] = valid[j] ? window_kb(g, w, e) : 0;
+    const int t = kb[j] / g.nbf;
+    koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 128 * g.nbf + (kb[j] - t * g.nbf);
     acc[j] = 0.0;
   }
 #pragma unroll 4
   for (int d = 0; d < 128; ++d) {
     const double qd = qs[d];
-    const double* kd = kcol + (int64_t)d * g.nkb;
+    const double* kd = p.kcache + (int64_t)d * g.nbf;
 #pragma unroll
-    for (int j = 0; j < M; ++j) acc[j] = fma(qd, kd[kb[j]], acc[j]);
+    for (int j = 0; j < M; ++j) acc[j] = fma(qd, kd[koff[j]], acc[j]);
   }
 
   if (p.scores) {  // every key block written once: -inf outside the window
@@ -271,7 +278,7 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
 }  // namespace
 
 hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStream_t stream) {
-  const dim3 grid(p.g.nqb + p.g.nkb, p.g.heads, batch);
+  const dim3 grid(p.g.nqb + (p.g.kv_frames - p.k_first) * p.g.nbf, p.g.heads, batch);
   if (block_tokens == 128)
     hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, stream, p);
   else

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LCSA_ABI_VERSION 2
+#define LCSA_ABI_VERSION 3
 
 typedef int32_t lcsa_status;
 #define LCSA_OK 0
@@ -57,6 +57,9 @@ typedef int32_t lcsa_status;
 #define LCSA_ERR_INTERNAL 8   /* allocation failure or unexpected state */
 
 #define LCSA_DTYPE_BF16 1
+
+/* Most KV-window frames a plan may have. */
+#define LCSA_MAX_KV_FRAMES 64
 
 /* Shape and control of one LCSA layer call.
  *  batch, heads       > 0.
@@ -130,6 +133,7 @@ typedef struct lcsa_plan_info {
   int64_t kv_tokens;
   uint64_t select_workspace_bytes;
   uint64_t attend_workspace_bytes; /* enough for any gfx950 device */
+  uint64_t kcache_slot_bytes;  /* pooled-K cache bytes per ring slot */
   double scale;                /* softmax scale actually used */
   double useful_flops;         /* 4 * head_dim * block_tokens^2 * nnz */
 } lcsa_plan_info;
@@ -207,6 +211,49 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
                         const int32_t* d_col_idx, int64_t nnz, const lcsa_tensor* o,
                         float* d_lse, void* d_workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Streaming KV storage.  In the streaming contract every chunk's queries
+ * attend to a KV window of the newest kv_frames latent frames (FlashVSR
+ * Inference skill page, "Non-Negotiable Streaming Contract": kv_ratio), and
+ * KV concatenation and pooling of that window are part of the attention glue
+ * (FlashVSR Hopper PR page, "What Was Actually Slow").  A frame ring avoids
+ * both copies: K and V live frame by frame in `slots` ring slots of two
+ * caller buffers (logical shape [batch, slots * grid_h * grid_w, heads,
+ * 128], lcsa_tensor strides as usual), each chunk writes only its new
+ * frames, and frame_slot[t] names the slot of window frame t (oldest first,
+ * t < kv_frames).  Slot indices must lie in [0, slots). */
+typedef struct lcsa_kv_ring {
+  int32_t slots;
+  int32_t frame_slot[LCSA_MAX_KV_FRAMES];
+} lcsa_kv_ring;
+
+/* Block selection over a frame ring with an incremental pooled-K cache.
+ * Same result as lcsa_select on the window's K laid out contiguously.
+ *  k_ring          the K ring (see lcsa_kv_ring), read only.
+ *  new_frames      0 .. kv_frames: the pooled K of the new_frames newest
+ *                  window frames is computed and stored in their slots'
+ *                  cache entries; the entries of the older window frames
+ *                  are used as they are, so they must hold the pooled K of
+ *                  the frames now in those slots (written by an earlier
+ *                  call with the same batch, heads and grid).
+ *  d_kcache        device double[slots * kcache_slot_bytes / 8], caller
+ *                  owned and kept between calls, 256-byte aligned; layout
+ *                  [slot][batch * heads][128][blocks_per_frame].
+ *  other arguments as lcsa_select (the workspace holds the pooled Q).
+ * Errors: as lcsa_select, plus INVALID (ring or new_frames out of range). */
+lcsa_status lcsa_select_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,
+                             const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
+                             int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                             void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention with K and V read from a frame ring; otherwise as
+ * lcsa_attend (same result as on the contiguous window).
+ * Errors: as lcsa_attend, plus INVALID (ring out of range). */
+lcsa_status lcsa_attend_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,
+                             const lcsa_tensor* v_ring, const lcsa_kv_ring* ring,
+                             const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
+                             const lcsa_tensor* o, float* d_lse, void* d_workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* lcsa_status_string(lcsa_status status);

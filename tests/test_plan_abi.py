@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lcsa.abi_version() == 2
+    assert lcsa.abi_version() == 3
     lib = ctypes.CDLL(lcsa.lib_path())
     lib.lcsa_status_string.restype = ctypes.c_char_p
     texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
@@ -75,6 +75,7 @@ def test_plan_matches_oracle_geometry(name):
     # room for one device-wide round of split pieces: 256 CUs x 8 waves
     bt = g.block_tokens
     assert inf["attend_workspace_bytes"] == 256 * (8 // (bt // 32)) * bt * (128 + 2) * 4
+    assert inf["kcache_slot_bytes"] == g.batch * g.heads * 128 * g.nbf * 8
     for qb in range(0, g.nqb, max(1, g.nqb // 37)):
         assert np.array_equal(p.window(qb), oracle.window(g, qb))
 
@@ -167,6 +168,41 @@ def test_entry_point_validation_statuses():
     big = lcsa.Plan.from_desc(dict(li.CONFIGS["first_2048x3840"], local_range=15))
     assert big.info["max_window"] > 1024
     assert _select(big, good, good) == 3                              # SHAPE: window limit
+
+
+def test_ring_entry_point_validation_statuses():
+    """Frame-ring arguments are checked on the host before any HIP call."""
+    p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])      # kv_frames 3
+    kvf = p.info["kv_frames"]
+    good = _fake_view()
+    lib = lcsa._lib
+    ws, wsb = 0x40000, p.info["select_workspace_bytes"]
+
+    def sel(ring, new=1, kc=0x80000):
+        r = ctypes.byref(ring) if ring is not None else None
+        return lib.lcsa_select_ring(p.handle, ctypes.byref(good), ctypes.byref(good), r, new, kc,
+                                    0x20000, 0x30000, None, ws, wsb, None)
+
+    def att(ring):
+        r = ctypes.byref(ring) if ring is not None else None
+        return lib.lcsa_attend_ring(p.handle, ctypes.byref(good), ctypes.byref(good),
+                                    ctypes.byref(good), r, 0x20000, 0x30000, 8, ctypes.byref(good),
+                                    None, None, 0, None)
+    ok = lcsa.kv_ring(4, [3, 0, 1])
+    assert sel(None) == 1                                            # NULL ring
+    assert sel(lcsa.kv_ring(0, [0, 0, 0])) == 2                      # no slots
+    assert sel(lcsa.kv_ring(4, [3, 4, 1])) == 2                      # slot out of range
+    assert sel(lcsa.kv_ring(4, [3, 0, -1])) == 2
+    assert sel(ok, new=kvf + 1) == 2 and sel(ok, new=-1) == 2        # new_frames
+    assert sel(ok, kc=0) == 1                                        # NULL cache
+    assert sel(ok, kc=0x80008) == 4                                  # ALIGN cache
+    assert att(None) == 1 and att(lcsa.kv_ring(2, [0, 1, 2])) == 2
+    if not torch.cuda.is_available():
+        assert sel(ok) == 6 and att(ok) == 6                         # DEVICE on CPU hosts
+    too_many = dict(li.CONFIGS["tiny"], q_frames=65, kv_ratio=0.0)
+    with pytest.raises(lcsa.LcsaError) as ei:
+        lcsa.Plan.from_desc(too_many)
+    assert ei.value.name == "LCSA_ERR_SHAPE"
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device status on CPU hosts")
