@@ -2,10 +2,11 @@
 //
 //  pool_kernel    mean of every query block of Q and key block of K, per head
 //                 (float64 sums of the bf16 values).
-//  select_kernel  one wave per CSR row (batch, head, query block): score the
-//                 pooled query against every pooled key block of its spatial
-//                 window, find the k-th best score, emit the kept blocks in
-//                 ascending order.
+//  select_kernel  one wave per (batch, head, spatial position, group of query
+//                 frames): score the pooled queries against every pooled key
+//                 block of their shared spatial window, then per CSR row find
+//                 the k-th best score and emit the kept blocks in ascending
+//                 order.
 //
 // Pooling and mask selection are the "attention glue" of the FlashVSR Hopper
 // PR page ("What Was Actually Slow"), with the mask emitted as CSR ("Rebuild
@@ -130,28 +131,34 @@ __device__ inline int wave_count(bool pred) {
   return __popcll(__builtin_amdgcn_ballot_w64(pred));
 }
 
-template <int M>
-__device__ void select_row(const SelectParams& p, const WindowBox& w, int b, int h, int tq, int pos,
-                           double* qs) {
+// One wave scores the rows of R query frames at one spatial position: they
+// share the window, so every pooled-key load feeds R dot products.  Then the
+// top-k of each row in turn.  Candidate e = lane + 64 j (j < M).
+template <int M, int R>
+__device__ void select_rows(const SelectParams& p, const WindowBox& w, int b, int h, int tq0,
+                            int nr, int pos, double (*qs)[128]) {
   const GridGeom& g = p.g;
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * g.heads + h;
-  const int qb = tq * g.nbf + pos;
-  const int64_t row = bh * g.nqb + qb;
 
-  // Pooled query of this row -> LDS (read back as broadcasts).
-  const double* qsrc = p.qbar + row * 128;
-  qs[lane] = qsrc[lane];
-  qs[lane + 64] = qsrc[lane + 64];
+  // Pooled queries of the rows -> LDS (read back as broadcasts).
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nr) {
+      const double* qsrc = p.qbar + (bh * g.nqb + (tq0 + r) * g.nbf + pos) * 128;
+      qs[r][lane] = qsrc[lane];
+      qs[r][lane + 64] = qsrc[lane + 64];
+    }
+  }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-  // Lane-per-candidate float64 scores: candidate e = lane + 64 j.  Pooled K
-  // of key block (t, pos) sits at kcache[kv_slot[t]][bh][d][pos].
+  // Float64 scores.  Pooled K of key block (t, pos) sits at
+  // kcache[kv_slot[t]][bh][d][pos].
   int kb[M];
   int64_t koff[M];
   bool valid[M];
-  double acc[M];
+  double acc[M][R];
   const int64_t bh_all = (int64_t)p.batch * g.heads;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
@@ -160,29 +167,25 @@ __device__ void select_row(const SelectParams& p, const WindowBox& w, int b, int
     kb[j] = valid[j] ? window_kb(g, w, e) : 0;
     const int t = kb[j] / g.nbf;
     koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 128 * g.nbf + (kb[j] - t * g.nbf);
-    acc[j] = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
   }
-#pragma unroll 4
+  // more channels in flight for narrow windows (loads are latency-bound)
+#pragma unroll (M <= 1 ? 8 : (M <= 4 ? 4 : 2))
   for (int d = 0; d < 128; ++d) {
-    const double qd = qs[d];
     const double* kd = p.kcache + (int64_t)d * g.nbf;
+    double kv[M];
 #pragma unroll
-    for (int j = 0; j < M; ++j) acc[j] = fma(qd, kd[koff[j]], acc[j]);
-  }
-
-  if (p.scores) {  // every key block written once: -inf outside the window
-    double* srow = p.scores + row * g.nkb;
-    for (int x = lane; x < g.nkb; x += 64) {
-      const int xt = x / g.nbf, xp = x - xt * g.nbf;
-      const int xy = xp / g.nbw, xx = xp - xy * g.nbw;
-      if (xy < w.y0 || xy > w.y1 || xx < w.x0 || xx > w.x1) srow[x] = -__builtin_huge_val();
+    for (int j = 0; j < M; ++j) kv[j] = kd[koff[j]];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const double qd = qs[r][d];
+#pragma unroll
+      for (int j = 0; j < M; ++j) acc[j][r] = fma(qd, kv[j], acc[j][r]);
     }
-#pragma unroll
-    for (int j = 0; j < M; ++j)
-      if (valid[j]) srow[kb[j]] = acc[j];
   }
 
-  // CSR offset of this row: rows run (b, h, frame, position); every frame
+  // CSR offset of these rows: rows run (b, h, frame, position); every frame
   // holds the same per-position counts min(k, |window(position)|).
   int lt = 0, all = 0;
   for (int q = lane; q < g.nbf; q += 64) {
@@ -196,83 +199,101 @@ __device__ void select_row(const SelectParams& p, const WindowBox& w, int b, int
     all += __shfl_xor(all, m);
   }
   const int keep = min(g.k, w.n);
-  const int64_t off = (bh * g.q_frames + tq) * (int64_t)all + lt;
-  if (lane == 0) {
-    p.row_ptr[row + 1] = (int32_t)(off + keep);
-    if (row == 0) p.row_ptr[0] = 0;
-  }
-
-  bool sel[M];
-  if (keep >= w.n) {
-#pragma unroll
-    for (int j = 0; j < M; ++j) sel[j] = valid[j];
-  } else {
-    uint64_t key[M];
-#pragma unroll
-    for (int j = 0; j < M; ++j) key[j] = valid[j] ? order_key(acc[j]) : 0ull;
-    // Largest T with #{key >= T} >= keep, decided bit by bit from the top.
-    // Invalid lanes hold key 0, which never reaches a trial value > 0.
-    uint64_t t = 0;
-    bool exact = false;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t trial = t | (1ull << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < M; ++j) cnt += wave_count(key[j] >= trial);
-      if (cnt >= keep) t = trial;
-      if (cnt == keep) {  // the set {key >= trial} is exactly the top keep
-        exact = true;
-        break;
-      }
-    }
-    if (exact) {
-#pragma unroll
-      for (int j = 0; j < M; ++j) sel[j] = valid[j] && key[j] >= t;
-    } else {
-      // t is the keep-th largest key; keys == t are admitted by index.
-      int need = keep;
-#pragma unroll
-      for (int j = 0; j < M; ++j) need -= wave_count(valid[j] && key[j] > t);
-      const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-      for (int j = 0; j < M; ++j) {
-        const bool tie = valid[j] && key[j] == t;
-        const uint64_t tm = __builtin_amdgcn_ballot_w64(tie);
-        const int rank = __popcll(tm & below);
-        sel[j] = (valid[j] && key[j] > t) || (tie && rank < need);
-        need -= __popcll(tm);
-        need = need < 0 ? 0 : need;
-      }
-    }
-  }
-
-  // Emit kept blocks in ascending candidate (= key block) order.
   const uint64_t below = (1ull << lane) - 1ull;
-  int base = 0;
+
 #pragma unroll
-  for (int j = 0; j < M; ++j) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(sel[j]);
-    if (sel[j]) p.col_idx[off + base + __popcll(m & below)] = kb[j];
-    base += __popcll(m);
+  for (int r = 0; r < R; ++r) {
+    if (r >= nr) break;
+    const int tq = tq0 + r;
+    const int64_t row = bh * g.nqb + tq * g.nbf + pos;
+    if (p.scores) {  // every key block written once: -inf outside the window
+      double* srow = p.scores + row * g.nkb;
+      for (int x = lane; x < g.nkb; x += 64) {
+        const int xt = x / g.nbf, xp = x - xt * g.nbf;
+        const int xy = xp / g.nbw, xx = xp - xy * g.nbw;
+        if (xy < w.y0 || xy > w.y1 || xx < w.x0 || xx > w.x1) srow[x] = -__builtin_huge_val();
+      }
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (valid[j]) srow[kb[j]] = acc[j][r];
+    }
+    const int64_t off = (bh * g.q_frames + tq) * (int64_t)all + lt;
+    if (lane == 0) {
+      p.row_ptr[row + 1] = (int32_t)(off + keep);
+      if (row == 0) p.row_ptr[0] = 0;
+    }
+
+    bool sel[M];
+    if (keep >= w.n) {
+#pragma unroll
+      for (int j = 0; j < M; ++j) sel[j] = valid[j];
+    } else {
+      uint64_t key[M];
+#pragma unroll
+      for (int j = 0; j < M; ++j) key[j] = valid[j] ? order_key(acc[j][r]) : 0ull;
+      // Largest T with #{key >= T} >= keep, decided bit by bit from the top.
+      // Invalid lanes hold key 0, which never reaches a trial value > 0.
+      uint64_t t = 0;
+      bool exact = false;
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t trial = t | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < M; ++j) cnt += wave_count(key[j] >= trial);
+        if (cnt >= keep) t = trial;
+        if (cnt == keep) {  // the set {key >= trial} is exactly the top keep
+          exact = true;
+          break;
+        }
+      }
+      if (exact) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) sel[j] = valid[j] && key[j] >= t;
+      } else {
+        // t is the keep-th largest key; keys == t are admitted by index.
+        int need = keep;
+#pragma unroll
+        for (int j = 0; j < M; ++j) need -= wave_count(valid[j] && key[j] > t);
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          const bool tie = valid[j] && key[j] == t;
+          const uint64_t tm = __builtin_amdgcn_ballot_w64(tie);
+          const int rank = __popcll(tm & below);
+          sel[j] = (valid[j] && key[j] > t) || (tie && rank < need);
+          need -= __popcll(tm);
+          need = need < 0 ? 0 : need;
+        }
+      }
+    }
+
+    // Emit kept blocks in ascending candidate (= key block) order.
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(sel[j]);
+      if (sel[j]) p.col_idx[off + base + __popcll(m & below)] = kb[j];
+      base += __popcll(m);
+    }
   }
 }
 
-// grid (ceil(q_frames / kSelectWaves), NBF, heads * batch); wave w of a
-// workgroup handles query frame blockIdx.x * kSelectWaves + w at spatial
-// position blockIdx.y.  The waves of a workgroup share one window, so their
-// pooled-key reads hit the same cache lines.
-template <int M>
+// grid (ceil(NBF / kSelectWaves) * ceil(q_frames / R), heads * batch); wave
+// w of a workgroup handles spatial position (x % pgroups) * kSelectWaves + w
+// and the R query frames of frame group x / pgroups.
+template <int M, int R>
 __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams p) {
-  __shared__ double qshare[kSelectWaves][128];
+  __shared__ double qshare[kSelectWaves][R][128];
   const GridGeom& g = p.g;
   const int wave = threadIdx.x >> 6;
-  const int tq = blockIdx.x * kSelectWaves + wave;
-  const int pos = blockIdx.y;
-  const int h = blockIdx.z % g.heads, b = blockIdx.z / g.heads;
-  if (tq >= g.q_frames) return;
+  const int pgroups = (g.nbf + kSelectWaves - 1) / kSelectWaves;
+  const int pos = (blockIdx.x % pgroups) * kSelectWaves + wave;
+  const int tq0 = (blockIdx.x / pgroups) * R;
+  const int h = blockIdx.y % g.heads, b = blockIdx.y / g.heads;
+  if (pos >= g.nbf) return;
+  const int nr = min(R, g.q_frames - tq0);
   const int by = pos / g.nbw, bx = pos - by * g.nbw;
   const WindowBox w = window_box(g, by, bx);
-  select_row<M>(p, w, b, h, tq, pos, qshare[wave]);
+  select_rows<M, R>(p, w, b, h, tq0, nr, pos, qshare[wave]);
 }
 
 }  // namespace
@@ -286,21 +307,45 @@ hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStre
   return hipGetLastError();
 }
 
+template <int M, int R>
+void launch_select_mr(const SelectParams& p, int batch, hipStream_t stream) {
+  const int pgroups = (p.g.nbf + kSelectWaves - 1) / kSelectWaves;
+  const int fgroups = (p.g.q_frames + R - 1) / R;
+  const dim3 grid(pgroups * fgroups, p.g.heads * batch);
+  hipLaunchKernelGGL((select_kernel<M, R>), grid, dim3(kSelectWaves * 64), 0, stream, p);
+}
+
+template <int M, int RMAX>
+void launch_select_m(const SelectParams& p, int batch, hipStream_t stream) {
+  // rows per wave: the frames there are, up to RMAX (register budget)
+  const int qf = p.g.q_frames;
+  if (qf <= 1 || RMAX == 1)
+    launch_select_mr<M, 1>(p, batch, stream);
+  else if (qf <= 2 || RMAX == 2)
+    launch_select_mr<M, (RMAX < 2 ? RMAX : 2)>(p, batch, stream);
+  else if (qf <= 4 || RMAX <= 4)
+    launch_select_mr<M, (RMAX < 4 ? RMAX : 4)>(p, batch, stream);
+  else if (qf <= 6 || RMAX <= 6)
+    launch_select_mr<M, (RMAX < 6 ? RMAX : 6)>(p, batch, stream);
+  else
+    launch_select_mr<M, RMAX>(p, batch, stream);
+}
+
 hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipStream_t stream) {
-  const dim3 grid((p.g.q_frames + kSelectWaves - 1) / kSelectWaves, p.g.nbf, p.g.heads * batch);
-  const dim3 block(kSelectWaves * 64);
-  // Candidates per lane, rounded up to a compiled width.
+  // Candidates per lane, rounded up to a compiled width; at most RMAX rows
+  // per wave so that the M x R float64 accumulators stay within about 100
+  // registers.
   const int m = (max_window + 63) / 64;
   if (m <= 1)
-    hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, stream, p);
+    launch_select_m<1, 8>(p, batch, stream);
   else if (m <= 4)
-    hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, stream, p);
+    launch_select_m<4, 8>(p, batch, stream);
   else if (m <= 8)
-    hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, stream, p);
+    launch_select_m<8, 6>(p, batch, stream);
   else if (m <= 12)
-    hipLaunchKernelGGL(select_kernel<12>, grid, block, 0, stream, p);
+    launch_select_m<12, 4>(p, batch, stream);
   else
-    hipLaunchKernelGGL(select_kernel<kMaxPerLane>, grid, block, 0, stream, p);
+    launch_select_m<kMaxPerLane, 2>(p, batch, stream);
   return hipGetLastError();
 }
 

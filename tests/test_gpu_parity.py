@@ -144,6 +144,29 @@ def test_attend_split_tail_matches_unsplit(name):
         compare_output(b, o_ref, f"{name} split")
 
 
+@pytest.mark.parametrize("shape", [(4, 16), (16, 4), (2, 32), (32, 4), (4, 32)])
+def test_explicit_block_shapes(shape):
+    """Explicit block shapes other than the automatic 8x16 / 16x8: the tile
+    loads and the window enumeration follow the block geometry."""
+    bh, bw = shape
+    desc = dict(li.CONFIGS["small_edges"], block_t=1, block_h=bh, block_w=bw, topk=6)
+    inp = li.generate(desc, seed=5)
+    q, k, v = (to_device_bf16(x) for x in (inp.q, inp.k, inp.v))
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci, sc = lcsa.select(plan, q, k, return_scores=True)
+    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+    o1 = lcsa.attend(plan, q, k, v, rp, ci, split_tail=False)
+    torch.cuda.synchronize()
+    g = oracle.geometry(desc)
+    rp_ref, ci_ref, s_ref = oracle.select(g, li.bf16_bits_to_f64(inp.q), li.bf16_bits_to_f64(inp.k))
+    check_mask(g, rp_ref, ci_ref, s_ref, rp.cpu().numpy(), ci.cpu().numpy())
+    o_ref, lse_ref = oracle.attend(g, _f32(inp.q), _f32(inp.k), _f32(inp.v),
+                                   rp.cpu().numpy().astype(np.int64), ci.cpu().numpy().astype(np.int64))
+    compare_output(bf16_to_np(o), o_ref, f"block {bh}x{bw}")
+    compare_output(bf16_to_np(o1), o_ref, f"block {bh}x{bw} unsplit")
+    assert float(np.abs(lse.cpu().numpy() - lse_ref).max()) <= LSE_TOL
+
+
 def test_attend_dense_special_case():
     """k = all key blocks with a covering window: plain dense attention."""
     desc = dict(li.CONFIGS["tiny"], topk=8)
