@@ -20,8 +20,6 @@ namespace lcsa {
 // Largest window (eligible key blocks of one query block) the select kernel
 // holds in LDS.
 constexpr int kMaxWindow = 1024;
-// Query frames scored together by one select workgroup.
-constexpr int kSelectFrames = 6;
 constexpr int kHeadDim = 128;
 // Compute units of the largest gfx950 device (MI355X, MI350X); sizes the
 // attention workspace for split rows.

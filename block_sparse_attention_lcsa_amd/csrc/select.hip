@@ -2,11 +2,11 @@
 //
 //  pool_kernel    mean of every query block of Q and key block of K, per head
 //                 (float64 sums of the bf16 values).
-//  select_kernel  one wave per (batch, head, spatial position, group of query
-//                 frames): score the pooled queries against every pooled key
-//                 block of their shared spatial window, then per CSR row find
-//                 the k-th best score and emit the kept blocks in ascending
-//                 order.
+//  select_kernel  one workgroup per (batch, head, spatial position, group of
+//                 query frames): its waves score the pooled queries against
+//                 every pooled key block of their shared spatial window into
+//                 an LDS table, then one wave per CSR row finds the k-th best
+//                 score and emits the kept blocks in ascending order.
 //
 // Pooling and mask selection are the "attention glue" of the FlashVSR Hopper
 // PR page ("What Was Actually Slow"), with the mask emitted as CSR ("Rebuild
@@ -22,7 +22,8 @@
 //
 // Top-k: scores map to order-preserving 64-bit keys; the k-th largest key is
 // found by deciding its bits from the top, each bit by one wave-wide count
-// (ballot + popcount) of the keys at or above the trial value.  Keys above
+// (ballot + popcount) of the keys at or above the trial value.  The bits all
+// keys of a row share (found from a wave-wide OR and AND) are skipped.  Keys above
 // it are kept; keys equal to it are kept in ascending block order until k
 // are kept (ties go to the lower block index).
 
@@ -131,59 +132,83 @@ __device__ inline int wave_count(bool pred) {
   return __popcll(__builtin_amdgcn_ballot_w64(pred));
 }
 
-// One wave scores the rows of R query frames at one spatial position: they
-// share the window, so every pooled-key load feeds R dot products.  Then the
-// top-k of each row in turn.  Candidate e = lane + 64 j (j < M).
+// Wave-wide OR and AND of a 64-bit value.
+__device__ inline void wave_or_and(uint64_t& o, uint64_t& a) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    o |= (uint64_t)__shfl_xor((unsigned long long)o, m);
+    a &= (uint64_t)__shfl_xor((unsigned long long)a, m);
+  }
+}
+
+// One workgroup takes the rows of up to R query frames at one spatial
+// position; they share the window.  Scores: wave w computes window
+// candidates e = lane + 64 (4 j + w) of every row into an LDS table, so each
+// pooled-key load feeds R dot products.  Top-k: wave w then takes rows w,
+// w + 4, ... and reads candidate e = lane + 64 j (j < M) of its row.
 template <int M, int R>
-__device__ void select_rows(const SelectParams& p, const WindowBox& w, int b, int h, int tq0,
-                            int nr, int pos, double (*qs)[128]) {
+__global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams p) {
+  constexpr int MW = (M + kSelectWaves - 1) / kSelectWaves;   // scoring slots per lane
+  __shared__ double qs[R][128];
+  __shared__ double sc[R][64 * M];
   const GridGeom& g = p.g;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pos = (int)(blockIdx.x % (unsigned)g.nbf);
+  const int tq0 = (int)(blockIdx.x / (unsigned)g.nbf) * R;
+  const int h = blockIdx.y % g.heads, b = blockIdx.y / g.heads;
+  const int nr = min(R, g.q_frames - tq0);
+  const int by = pos / g.nbw, bx = pos - by * g.nbw;
+  const WindowBox w = window_box(g, by, bx);
   const int64_t bh = (int64_t)b * g.heads + h;
 
   // Pooled queries of the rows -> LDS (read back as broadcasts).
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r < nr) {
-      const double* qsrc = p.qbar + (bh * g.nqb + (tq0 + r) * g.nbf + pos) * 128;
-      qs[r][lane] = qsrc[lane];
-      qs[r][lane + 64] = qsrc[lane + 64];
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int i = tid; i < nr * 128; i += kSelectWaves * 64)
+    qs[i >> 7][i & 127] = p.qbar[(bh * g.nqb + (int64_t)(tq0 + (i >> 7)) * g.nbf + pos) * 128 + (i & 127)];
+  __syncthreads();
 
-  // Float64 scores.  Pooled K of key block (t, pos) sits at
-  // kcache[kv_slot[t]][bh][d][pos].
-  int kb[M];
-  int64_t koff[M];
-  bool valid[M];
-  double acc[M][R];
-  const int64_t bh_all = (int64_t)p.batch * g.heads;
+  // Float64 scores.  Pooled K of key block (t, pos') sits at
+  // kcache[kv_slot[t]][bh][d][pos'].
+  if (64 * wave < w.n) {
+    int64_t koff[MW];
+    bool valid[MW];
+    double acc[MW][R];
+    const int64_t bh_all = (int64_t)p.batch * g.heads;
 #pragma unroll
-  for (int j = 0; j < M; ++j) {
-    const int e = lane + 64 * j;
-    valid[j] = e < w.n;
-    kb[j] = valid[j] ? window_kb(g, w, e) : 0;
-    const int t = kb[j] / g.nbf;
-    koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 128 * g.nbf + (kb[j] - t * g.nbf);
+    for (int j = 0; j < MW; ++j) {
+      const int e = lane + 64 * (kSelectWaves * j + wave);
+      valid[j] = e < w.n;
+      const int kb = valid[j] ? window_kb(g, w, e) : 0;
+      const int t = kb / g.nbf;
+      koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 128 * g.nbf + (kb - t * g.nbf);
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
-  }
-  // more channels in flight for narrow windows (loads are latency-bound)
-#pragma unroll (M <= 1 ? 8 : (M <= 4 ? 4 : 2))
-  for (int d = 0; d < 128; ++d) {
-    const double* kd = p.kcache + (int64_t)d * g.nbf;
-    double kv[M];
+      for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
+    }
+    // more channels in flight when a lane has few candidates (latency-bound)
+#pragma unroll (MW <= 1 ? 8 : 4)
+    for (int d = 0; d < 128; ++d) {
+      const double* kd = p.kcache + (int64_t)d * g.nbf;
+      double kv[MW];
 #pragma unroll
-    for (int j = 0; j < M; ++j) kv[j] = kd[koff[j]];
+      for (int j = 0; j < MW; ++j) kv[j] = kd[koff[j]];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const double qd = qs[r][d];
+      for (int r = 0; r < R; ++r) {
+        const double qd = qs[r][d];
 #pragma unroll
-      for (int j = 0; j < M; ++j) acc[j][r] = fma(qd, kv[j], acc[j][r]);
+        for (int j = 0; j < MW; ++j) acc[j][r] = fma(qd, kv[j], acc[j][r]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MW; ++j) {
+      if (valid[j]) {
+        const int e = lane + 64 * (kSelectWaves * j + wave);
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r][e] = acc[j][r];
+      }
     }
   }
+  __syncthreads();
+  if (wave >= nr) return;
 
   // CSR offset of these rows: rows run (b, h, frame, position); every frame
   // holds the same per-position counts min(k, |window(position)|).
@@ -200,12 +225,21 @@ __device__ void select_rows(const SelectParams& p, const WindowBox& w, int b, in
   }
   const int keep = min(g.k, w.n);
   const uint64_t below = (1ull << lane) - 1ull;
-
+  int kb[M];
+  bool valid[M];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r >= nr) break;
+  for (int j = 0; j < M; ++j) {
+    const int e = lane + 64 * j;
+    valid[j] = e < w.n;
+    kb[j] = valid[j] ? window_kb(g, w, e) : 0;
+  }
+
+  for (int r = wave; r < nr; r += kSelectWaves) {
     const int tq = tq0 + r;
     const int64_t row = bh * g.nqb + tq * g.nbf + pos;
+    double s[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) s[j] = valid[j] ? sc[r][lane + 64 * j] : 0.0;
     if (p.scores) {  // every key block written once: -inf outside the window
       double* srow = p.scores + row * g.nkb;
       for (int x = lane; x < g.nkb; x += 64) {
@@ -215,7 +249,7 @@ __device__ void select_rows(const SelectParams& p, const WindowBox& w, int b, in
       }
 #pragma unroll
       for (int j = 0; j < M; ++j)
-        if (valid[j]) srow[kb[j]] = acc[j][r];
+        if (valid[j]) srow[kb[j]] = s[j];
     }
     const int64_t off = (bh * g.q_frames + tq) * (int64_t)all + lt;
     if (lane == 0) {
@@ -229,13 +263,23 @@ __device__ void select_rows(const SelectParams& p, const WindowBox& w, int b, in
       for (int j = 0; j < M; ++j) sel[j] = valid[j];
     } else {
       uint64_t key[M];
+      uint64_t kor = 0ull, kand = ~0ull;
 #pragma unroll
-      for (int j = 0; j < M; ++j) key[j] = valid[j] ? order_key(acc[j][r]) : 0ull;
-      // Largest T with #{key >= T} >= keep, decided bit by bit from the top.
-      // Invalid lanes hold key 0, which never reaches a trial value > 0.
-      uint64_t t = 0;
+      for (int j = 0; j < M; ++j) {
+        key[j] = valid[j] ? order_key(s[j]) : 0ull;
+        kor |= valid[j] ? key[j] : 0ull;
+        kand &= valid[j] ? key[j] : ~0ull;
+      }
+      wave_or_and(kor, kand);
+      // Every valid key shares the bits above the highest bit where two of
+      // them differ, so the bisection starts there.  Largest T with
+      // #{key >= T} >= keep, decided bit by bit from the top.  Invalid lanes
+      // hold key 0, which never reaches a trial value > 0.
+      const uint64_t diff = kor ^ kand;
+      const int hb = diff ? 63 - __clzll(diff) : -1;
+      uint64_t t = hb >= 63 ? 0ull : kand & ~((2ull << hb) - 1ull);
       bool exact = false;
-      for (int bit = 63; bit >= 0; --bit) {
+      for (int bit = hb; bit >= 0; --bit) {
         const uint64_t trial = t | (1ull << bit);
         int cnt = 0;
 #pragma unroll
@@ -277,25 +321,6 @@ __device__ void select_rows(const SelectParams& p, const WindowBox& w, int b, in
   }
 }
 
-// grid (ceil(NBF / kSelectWaves) * ceil(q_frames / R), heads * batch); wave
-// w of a workgroup handles spatial position (x % pgroups) * kSelectWaves + w
-// and the R query frames of frame group x / pgroups.
-template <int M, int R>
-__global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams p) {
-  __shared__ double qshare[kSelectWaves][R][128];
-  const GridGeom& g = p.g;
-  const int wave = threadIdx.x >> 6;
-  const int pgroups = (g.nbf + kSelectWaves - 1) / kSelectWaves;
-  const int pos = (blockIdx.x % pgroups) * kSelectWaves + wave;
-  const int tq0 = (blockIdx.x / pgroups) * R;
-  const int h = blockIdx.y % g.heads, b = blockIdx.y / g.heads;
-  if (pos >= g.nbf) return;
-  const int nr = min(R, g.q_frames - tq0);
-  const int by = pos / g.nbw, bx = pos - by * g.nbw;
-  const WindowBox w = window_box(g, by, bx);
-  select_rows<M, R>(p, w, b, h, tq0, nr, pos, qshare[wave]);
-}
-
 }  // namespace
 
 hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStream_t stream) {
@@ -309,19 +334,18 @@ hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStre
 
 template <int M, int R>
 void launch_select_mr(const SelectParams& p, int batch, hipStream_t stream) {
-  const int pgroups = (p.g.nbf + kSelectWaves - 1) / kSelectWaves;
   const int fgroups = (p.g.q_frames + R - 1) / R;
-  const dim3 grid(pgroups * fgroups, p.g.heads * batch);
+  const dim3 grid(p.g.nbf * fgroups, p.g.heads * batch);
   hipLaunchKernelGGL((select_kernel<M, R>), grid, dim3(kSelectWaves * 64), 0, stream, p);
 }
 
 template <int M, int RMAX>
 void launch_select_m(const SelectParams& p, int batch, hipStream_t stream) {
-  // rows per wave: the frames there are, up to RMAX (register budget)
+  // rows per workgroup: the query frames there are, up to RMAX
   const int qf = p.g.q_frames;
-  if (qf <= 1 || RMAX == 1)
+  if (qf <= 1)
     launch_select_mr<M, 1>(p, batch, stream);
-  else if (qf <= 2 || RMAX == 2)
+  else if (qf <= 2 || RMAX <= 2)
     launch_select_mr<M, (RMAX < 2 ? RMAX : 2)>(p, batch, stream);
   else if (qf <= 4 || RMAX <= 4)
     launch_select_mr<M, (RMAX < 4 ? RMAX : 4)>(p, batch, stream);
@@ -332,20 +356,25 @@ void launch_select_m(const SelectParams& p, int batch, hipStream_t stream) {
 }
 
 hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipStream_t stream) {
-  // Candidates per lane, rounded up to a compiled width; at most RMAX rows
-  // per wave so that the M x R float64 accumulators stay within about 100
-  // registers.
+  // Candidates per lane in the top-k, rounded up to a compiled width; R x M
+  // at most 64 keeps the LDS score table within 32 KiB.
   const int m = (max_window + 63) / 64;
   if (m <= 1)
     launch_select_m<1, 8>(p, batch, stream);
+  else if (m <= 2)
+    launch_select_m<2, 8>(p, batch, stream);
+  else if (m <= 3)
+    launch_select_m<3, 8>(p, batch, stream);
   else if (m <= 4)
     launch_select_m<4, 8>(p, batch, stream);
+  else if (m <= 6)
+    launch_select_m<6, 8>(p, batch, stream);
   else if (m <= 8)
-    launch_select_m<8, 6>(p, batch, stream);
+    launch_select_m<8, 8>(p, batch, stream);
   else if (m <= 12)
     launch_select_m<12, 4>(p, batch, stream);
   else
-    launch_select_m<kMaxPerLane, 2>(p, batch, stream);
+    launch_select_m<kMaxPerLane, 4>(p, batch, stream);
   return hipGetLastError();
 }
 
