@@ -420,16 +420,19 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   }
 }
 
-// Merge of split rows: one workgroup per split row, thread t handles query
-// t / 2 and channels 64 * (t % 2) .. +63.  Pieces hold O and the row sum
-// against their own reference m (log2 units); the merge rescales each to the
-// largest m.  A row whose pieces hold no valid block gives O = 0, LSE = -inf.
+// Merge of split rows: workgroup (x, y) takes split row x, queries 16 y ..
+// 16 y + 15; thread t handles query 16 y + t / 16 and channels 8 (t % 16) ..
+// +7, so 16 lanes read one query's 512-byte partial row.  Pieces hold O and
+// the row sum against their own reference m (log2 units); the merge rescales
+// each to the largest m.  A row whose pieces hold no valid block gives O = 0,
+// LSE = -inf.
+constexpr int kMergeThreads = 256;
 template <int BT>
-__global__ void __launch_bounds__(BT * 2) attend_merge_kernel(AttendParams p) {
+__global__ void __launch_bounds__(kMergeThreads) attend_merge_kernel(AttendParams p) {
   const GridGeom& g = p.g;
   const int64_t tr = blockIdx.x;
   const int64_t row = p.full_rows + tr;
-  const int t = threadIdx.x, qi = t >> 1, c0 = (t & 1) * 64;
+  const int t = threadIdx.x, qi = (int)blockIdx.y * 16 + (t >> 4), c0 = (t & 15) * 8;
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;
   const int h = (int)(bh % g.heads);
@@ -442,9 +445,9 @@ __global__ void __launch_bounds__(BT * 2) attend_merge_kernel(AttendParams p) {
 
   float m = -__builtin_huge_valf();
   for (int pc = 0; pc < p.pieces; ++pc) m = fmaxf(m, ml[((tr * p.pieces + pc) * BT + qi) * 2]);
-  float acc[64];
+  float acc[8];
 #pragma unroll
-  for (int c = 0; c < 64; ++c) acc[c] = 0.0f;
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
   float l = 0.0f;
   if (m > -__builtin_huge_valf()) {
     for (int pc = 0; pc < p.pieces; ++pc) {
@@ -454,7 +457,7 @@ __global__ void __launch_bounds__(BT * 2) attend_merge_kernel(AttendParams p) {
       l = fmaf(w, mlp.y, l);
       const float4* src = reinterpret_cast<const float4*>(p.part + (it * BT + qi) * 128 + c0);
 #pragma unroll
-      for (int c4 = 0; c4 < 16; ++c4) {
+      for (int c4 = 0; c4 < 2; ++c4) {
         const float4 x = src[c4];
         acc[4 * c4 + 0] = fmaf(w, x.x, acc[4 * c4 + 0]);
         acc[4 * c4 + 1] = fmaf(w, x.y, acc[4 * c4 + 1]);
@@ -465,19 +468,16 @@ __global__ void __launch_bounds__(BT * 2) attend_merge_kernel(AttendParams p) {
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   uint16_t* orow = p.o + (int64_t)b * p.o_sb + qtok * p.o_ss + (int64_t)h * p.o_sh + c0;
+  uint4 w;
+  uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
 #pragma unroll
-  for (int c8 = 0; c8 < 8; ++c8) {
-    uint4 w;
-    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      f32x2_t x;
-      x[0] = acc[8 * c8 + 2 * k2] * inv;
-      x[1] = acc[8 * c8 + 2 * k2 + 1] * inv;
-      wp[k2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
-    }
-    *reinterpret_cast<uint4*>(orow + 8 * c8) = w;
+  for (int k2 = 0; k2 < 4; ++k2) {
+    f32x2_t x;
+    x[0] = acc[2 * k2] * inv;
+    x[1] = acc[2 * k2 + 1] * inv;
+    wp[k2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
   }
+  *reinterpret_cast<uint4*>(orow) = w;
   if (p.lse && c0 == 0) {
     const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * 0.69314718055994531f : -__builtin_huge_valf();
     p.lse[((int64_t)b * g.heads + h) * g.q_tokens + qtok] = lse;
@@ -492,7 +492,8 @@ hipError_t launch_bt(const AttendParams& p, hipStream_t stream) {
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 0) return e;
-  hipLaunchKernelGGL(attend_merge_kernel<BT>, dim3((unsigned)split), dim3(BT * 2), 0, stream, p);
+  hipLaunchKernelGGL(attend_merge_kernel<BT>, dim3((unsigned)split, BT / 16), dim3(kMergeThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
