@@ -30,9 +30,11 @@
 //  * Lazy rescale: the running max only moves when some lane's block max
 //    exceeds it by more than 2^8; exp2 arguments stay <= 8, and O and the row
 //    sum share the same stale reference, so the result is unchanged.
-//  * Rows are laid out so each XCD (workgroup id mod 8) walks a contiguous
-//    range of rows (same head, neighbouring query blocks), which share most
-//    of their selected key blocks in that XCD's L2.
+//  * Rows are visited head by head, in square tiles of block positions with
+//    all query frames of a tile together, and each XCD (workgroup id mod 8)
+//    walks a contiguous range of that order: the rows in flight on an XCD
+//    have overlapping windows and select largely the same key blocks, which
+//    then stay in that XCD's L2 and the memory-side cache.
 
 #include <hip/hip_runtime.h>
 
@@ -54,6 +56,26 @@ constexpr float kLazyRescale = 8.0f;   // log2 units
 constexpr int kXcds = 8;
 
 __device__ inline uint4 load16(const uint16_t* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
+
+// CSR row at enumeration index e of the visiting order (batch*head, tile row,
+// tile, query frame, position in the tile); tiles are tile x tile block
+// positions, clipped at the right and bottom edges of the frame.
+__device__ inline int64_t visit_row(const GridGeom& g, int tile, int64_t e) {
+  const int64_t bh = e / g.nqb;
+  int r = (int)(e - bh * g.nqb);
+  const int qf = g.q_frames;
+  const int band = tile * g.nbw * qf;            // indices per full tile row
+  const int ty = r / band;
+  r -= ty * band;
+  const int th = min(tile, g.nbh - ty * tile);
+  const int tx = r / (th * tile * qf);
+  r -= tx * th * tile * qf;
+  const int tw = min(tile, g.nbw - tx * tile);
+  const int tq = r / (th * tw);
+  const int pp = r - tq * th * tw;
+  const int py = pp / tw, px = pp - py * tw;
+  return bh * g.nqb + (int64_t)tq * g.nbf + (ty * tile + py) * g.nbw + tx * tile + px;
+}
 __device__ inline bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // 16-byte chunk swizzles of the row-major [key][128] tiles (16 chunks per
@@ -148,8 +170,8 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
 
   // Work item: workgroups [0, full_rows) take whole rows, in an XCD-aware
   // order (workgroup ids go round-robin over the XCDs; XCD x gets the
-  // contiguous row range [start_x, start_x + count_x)); later workgroups
-  // take piece `piece` of a split row.
+  // contiguous range [start_x, start_x + count_x) of the visiting order);
+  // later workgroups take piece `piece` of a split row.
   int64_t row, item = -1;
   int piece = -1;
   {
@@ -163,6 +185,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
       row = n + item / p.pieces;
       piece = (int)(item % p.pieces);
     }
+    row = visit_row(g, p.tile, row);
   }
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;
@@ -431,7 +454,7 @@ template <int BT>
 __global__ void __launch_bounds__(kMergeThreads) attend_merge_kernel(AttendParams p) {
   const GridGeom& g = p.g;
   const int64_t tr = blockIdx.x;
-  const int64_t row = p.full_rows + tr;
+  const int64_t row = visit_row(g, p.tile, p.full_rows + tr);
   const int t = threadIdx.x, qi = (int)blockIdx.y * 16 + (t >> 4), c0 = (t & 15) * 8;
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;

@@ -214,10 +214,10 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   // a second kernel.
   int64_t full_rows = in.rows;
   int pieces = 1;
+  int cus = 0;
+  if ((st = device_cus(&cus))) return st;
+  const int64_t slots = static_cast<int64_t>(cus) * attend_groups_per_cu(in.block_tokens);
   if (d_workspace) {
-    int cus = 0;
-    if ((st = device_cus(&cus))) return st;
-    const int64_t slots = static_cast<int64_t>(cus) * attend_groups_per_cu(in.block_tokens);
     const int64_t tail = in.rows % slots;
     if (tail > 0) {
       int64_t want = slots / tail;
@@ -251,6 +251,7 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   ap.rows = in.rows;
   ap.full_rows = full_rows;
   ap.pieces = pieces;
+  ap.tile = attend_tile(slots, plan->desc.q_frames, in.nbh, in.nbw);
   ap.part = static_cast<float*>(d_workspace);
   ap.scale_log2 = static_cast<float>(in.scale * 1.4426950408889634);
   const hipError_t e = launch_attend(ap, in.block_tokens, static_cast<hipStream_t>(stream));

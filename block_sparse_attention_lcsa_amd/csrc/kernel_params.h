@@ -65,6 +65,10 @@ struct AttendParams {
   // unnormalised partial result to `part` for the merge kernel.
   int64_t full_rows;
   int32_t pieces;
+  // Visiting order of the rows: enumeration index e runs over (batch*head,
+  // tile of tile x tile block positions, query frame, position in the tile);
+  // work items above are enumeration indices.
+  int32_t tile;
   float* part;           // [items][BT][128] partial O, then [items][BT][2] (m, l)
   float scale_log2;      // softmax scale * log2(e)
 };

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "kernel_params.h"
 
 namespace lcsa {
@@ -18,5 +20,15 @@ inline int64_t attend_piece_bytes(int block_tokens) {
 }
 // Workgroups of the attention kernel resident on one CU (eight waves).
 inline int attend_groups_per_cu(int block_tokens) { return 8 / (block_tokens / 32); }
+// Side of the square position tiles of the attention visiting order: one
+// tile with all its query frames is about one XCD's resident workgroups
+// (slots / 8).  A side covering the frame gives plain row order.
+inline int attend_tile(int64_t slots, int q_frames, int nbh, int nbw) {
+  const double per_xcd = static_cast<double>(slots / 8);
+  int t = static_cast<int>(std::sqrt(per_xcd / (q_frames > 0 ? q_frames : 1)) + 0.5);
+  const int side = nbh > nbw ? nbh : nbw;
+  t = t < 1 ? 1 : t;
+  return t > side ? side : t;
+}
 
 }  // namespace lcsa
