@@ -22,10 +22,10 @@
 //
 // Top-k: scores map to order-preserving 64-bit keys; the k-th largest key is
 // found by deciding its bits from the top, each bit by one wave-wide count
-// (ballot + popcount) of the keys at or above the trial value.  The bits all
-// keys of a row share (found from a wave-wide OR and AND) are skipped.  Keys above
+// (ballot + popcount) of the keys at or above the trial value.  Keys above
 // it are kept; keys equal to it are kept in ascending block order until k
-// are kept (ties go to the lower block index).
+// are kept (ties go to the lower block index).  The bits that all keys of a
+// row share (found from a wave-wide OR and AND) need no count.
 
 #include <hip/hip_runtime.h>
 
@@ -356,8 +356,9 @@ void launch_select_m(const SelectParams& p, int batch, hipStream_t stream) {
 }
 
 hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipStream_t stream) {
-  // Candidates per lane in the top-k, rounded up to a compiled width; R x M
-  // at most 64 keeps the LDS score table within 32 KiB.
+  // Candidates per lane in the top-k, rounded up to a compiled width; up to
+  // 8 rows per workgroup (the LDS score table is R x 64 M float64, at most
+  // 64 KiB), since every row shares the workgroup's pooled-K loads.
   const int m = (max_window + 63) / 64;
   if (m <= 1)
     launch_select_m<1, 8>(p, batch, stream);
@@ -372,9 +373,9 @@ hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipSt
   else if (m <= 8)
     launch_select_m<8, 8>(p, batch, stream);
   else if (m <= 12)
-    launch_select_m<12, 4>(p, batch, stream);
+    launch_select_m<12, 8>(p, batch, stream);
   else
-    launch_select_m<kMaxPerLane, 4>(p, batch, stream);
+    launch_select_m<kMaxPerLane, 8>(p, batch, stream);
   return hipGetLastError();
 }
 
