@@ -27,9 +27,11 @@
 //    spread over the MFMA loop (one per step) instead of issued in a burst.
 //    Barriers are raw s_barrier with explicit vmcnt waits, so in-flight
 //    tile loads are not drained at every barrier.
-//  * Lazy rescale: the running max only moves when some lane's block max
-//    exceeds it by more than 2^8; exp2 arguments stay <= 8, and O and the row
-//    sum share the same stale reference, so the result is unchanged.
+//  * Max-free softmax: P is computed against the running reference first;
+//    only when some lane's partial row sum leaves [0, 2^16] (a row's first
+//    block, or scores far above the reference) is the block max taken, O and
+//    the row sum rescaled and P recomputed.  O and the row sum share the
+//    reference, so the result is unchanged; P <= 2^16 keeps sums finite.
 //  * Rows are visited head by head, in square tiles of block positions with
 //    all query frames of a tile together, and each XCD (workgroup id mod 8)
 //    walks a contiguous range of that order: the rows in flight on an XCD
@@ -52,7 +54,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-constexpr float kLazyRescale = 8.0f;   // log2 units
+// Largest partial row sum (64 values of P per lane) accepted without moving
+// the softmax reference.
+constexpr float kSumBound = 65536.0f;
 constexpr int kXcds = 8;
 
 __device__ inline uint4 load16(const uint16_t* ptr) { return *reinterpret_cast<const uint4*>(ptr); }
@@ -323,20 +327,56 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     const char* ksrc = kbase + block_offset(col_idx[nx < end ? nx : it], row_stride_k);
 
     // ---- online softmax (one query per lane, keys split over lane ^ 32)
-    // Independent max chains per key tile keep the reduction short.
-    float mt[T::kKeyTiles];
+    // P = exp2(S * scale*log2(e) - m_run) rounded to bf16 pairs; the row sum
+    // adds exactly these rounded values (dot with (1, 1)), one chain per key
+    // tile.  The reference m_run moves only when some lane's partial row sum
+    // leaves [0, kSumBound]: on a row's first block (m_run = -inf gives
+    // infinite sums) and when a block's scores rise far above m_run.  Then
+    // the block max is taken, O and the row sum are rescaled, and P is
+    // recomputed.  Otherwise no max is needed: P <= kSumBound keeps every
+    // accumulation finite, and O and the row sum share the reference.
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8_t pb[T::kKeyTiles][2];
+    auto make_p = [&](const float neg_m) __attribute__((always_inline)) {
+      float rs[T::kKeyTiles];
 #pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt) {
-      mt[kt] = fmaxf(s[kt][0], s[kt][1]);
+      for (int kt = 0; kt < T::kKeyTiles; ++kt) {
+        rs[kt] = 0.0f;
+        bf16x2_t pp[8];
 #pragma unroll
-      for (int r = 2; r < 16; ++r) mt[kt] = fmaxf(mt[kt], s[kt][r]);
-    }
-    float mx = mt[0];
+        for (int r2 = 0; r2 < 8; ++r2) {
+          f32x2_t e;
+          e[0] = __builtin_amdgcn_exp2f(fmaf(s[kt][2 * r2], sl2, neg_m));
+          e[1] = __builtin_amdgcn_exp2f(fmaf(s[kt][2 * r2 + 1], sl2, neg_m));
+          pp[r2] = __builtin_convertvector(e, bf16x2_t);
+          rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(pp[r2], ones, rs[kt], false);
+        }
+        pb[kt][0] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                            __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+        pb[kt][1] = __builtin_shufflevector(__builtin_shufflevector(pp[4], pp[5], 0, 1, 2, 3),
+                                            __builtin_shufflevector(pp[6], pp[7], 0, 1, 2, 3),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      float sum = rs[0];
 #pragma unroll
-    for (int kt = 1; kt < T::kKeyTiles; ++kt) mx = fmaxf(mx, mt[kt]);
-    const float m_blk = pair_max(mx) * sl2;
-    if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_run, m_blk);
+      for (int kt = 1; kt < T::kKeyTiles; ++kt) sum += rs[kt];
+      return sum;
+    };
+    float rsum = make_p(-m_run);
+    if (__builtin_amdgcn_ballot_w64(!(rsum <= kSumBound)) != 0) {
+      // Independent max chains per key tile keep the reduction short.
+      float mt[T::kKeyTiles];
+#pragma unroll
+      for (int kt = 0; kt < T::kKeyTiles; ++kt) {
+        mt[kt] = fmaxf(s[kt][0], s[kt][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mt[kt] = fmaxf(mt[kt], s[kt][r]);
+      }
+      float mx = mt[0];
+#pragma unroll
+      for (int kt = 1; kt < T::kKeyTiles; ++kt) mx = fmaxf(mx, mt[kt]);
+      const float m_new = fmaxf(m_run, pair_max(mx) * sl2);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -344,34 +384,9 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      rsum = make_p(-m_run);
     }
-    const float neg_m = -m_run;
-    // P = exp2(S * scale*log2(e) - m) rounded to bf16 pairs; the row sum adds
-    // exactly these rounded values (dot with (1, 1)), one chain per key tile.
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x8_t pb[T::kKeyTiles][2];
-    float rs[T::kKeyTiles];
-#pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt) {
-      rs[kt] = 0.0f;
-      bf16x2_t pp[8];
-#pragma unroll
-      for (int r2 = 0; r2 < 8; ++r2) {
-        f32x2_t e;
-        e[0] = __builtin_amdgcn_exp2f(fmaf(s[kt][2 * r2], sl2, neg_m));
-        e[1] = __builtin_amdgcn_exp2f(fmaf(s[kt][2 * r2 + 1], sl2, neg_m));
-        pp[r2] = __builtin_convertvector(e, bf16x2_t);
-        rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(pp[r2], ones, rs[kt], false);
-      }
-      pb[kt][0] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                          __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                          0, 1, 2, 3, 4, 5, 6, 7);
-      pb[kt][1] = __builtin_shufflevector(__builtin_shufflevector(pp[4], pp[5], 0, 1, 2, 3),
-                                          __builtin_shufflevector(pp[6], pp[7], 0, 1, 2, 3),
-                                          0, 1, 2, 3, 4, 5, 6, 7);
-    }
-#pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt) l_run += rs[kt];
+    l_run += rsum;
 
     wait_vmcnt<0>();          // V(it) landed (the only loads in flight)
     barrier_raw();
