@@ -319,7 +319,6 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
         }
       }
     }
-    barrier_raw();            // every wave has read K(it)
     const int nx = next_valid(it + 1);
     // K(nx) is issued one load per PV step below (after the V barrier, when
     // every wave is done with K(it)); on the last block the current block is
@@ -389,7 +388,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     l_run += rsum;
 
     wait_vmcnt<0>();          // V(it) landed (the only loads in flight)
-    barrier_raw();
+    barrier_raw();            // ... everyone's; every wave is past S, so K(it) is free
 
     // ---- O^T += V^T P^T
 #pragma unroll
