@@ -216,6 +216,49 @@ def test_attend_caller_csr_edge_rows():
     assert np.all(bf16_to_np(o)[0, q_empty, 0, :] == 0)
 
 
+@pytest.mark.parametrize("order", ["rising", "falling", "random"])
+def test_attend_softmax_reference_moves(order):
+    """Key blocks scaled by factors 1 .. 256 so that block score maxima climb
+    (rising), fall (falling) or jump about (random) along every row's block
+    list, each row holding every key block in ascending order.  Rising and
+    random scores move the softmax reference again and again inside a row
+    (the branch that takes the block max, rescales O and the row sum, and
+    recomputes P); falling scores leave later blocks near underflow.  A move
+    happens only when the new block outweighs the earlier ones by about 2^10,
+    so this guards the branch against gross failure (P left against the old
+    reference, infinities, NaN), not the rescale factor's last bits."""
+    name = "small_edges"
+    desc, inp = host_inputs(name)
+    g = oracle.geometry(desc)
+    plan = lcsa.Plan.from_desc(desc)
+    nkb = g.nkb
+    if order == "rising":
+        f = 2.0 ** (8.0 * np.arange(nkb) / (nkb - 1))
+    elif order == "falling":
+        f = 2.0 ** (8.0 * np.arange(nkb)[::-1] / (nkb - 1))
+    else:
+        f = 2.0 ** np.random.default_rng(5).uniform(0.0, 8.0, nkb)
+    k32 = _f32(inp.k).copy()
+    for kb in range(nkb):
+        k32[:, oracle.block_tokens(g, kb)] *= np.float32(f[kb])
+    k_bits = li.f32_to_bf16_bits(k32)
+    rows = plan.info["rows"]
+    rp_h = (np.arange(rows + 1) * nkb).astype(np.int64)
+    ci_h = np.tile(np.arange(nkb), rows).astype(np.int64)
+    q = to_device_bf16(inp.q)
+    k = to_device_bf16(k_bits)
+    v = to_device_bf16(inp.v)
+    rp_d = torch.from_numpy(rp_h.astype(np.int32)).cuda()
+    ci_d = torch.from_numpy(ci_h.astype(np.int32)).cuda()
+    o, lse = lcsa.attend(plan, q, k, v, rp_d, ci_d, return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attend(g, _f32(inp.q), _f32(k_bits), _f32(inp.v), rp_h, ci_h)
+    say(f"  {order}: LSE range {float(lse_ref.min()):.1f} .. {float(lse_ref.max()):.1f}")
+    compare_output(bf16_to_np(o), o_ref, f"reference moves ({order})")
+    lse_h = lse.cpu().numpy()
+    assert np.all(np.abs(lse_h - lse_ref) <= LSE_TOL * np.maximum(1.0, np.abs(lse_ref)))
+
+
 def test_strided_views_and_kv_cache_window():
     """Q/K/V as slices of a packed QKV tensor, O written into a strided view,
     and K/V of a streaming call as a window of a longer cache: bitwise equal
