@@ -31,19 +31,20 @@ struct View {
   int64_t sb, ss, sh;    // strides in elements
 };
 
-// Pooled K lives per storage frame: kcache[slot][B*H][128][NBF].
+// Pooled K lives per storage frame, channel pairs innermost:
+// kcache[slot][B*H][64][NBF][2] holds channel 2c + e of position p at [c][p][e].
 struct PoolParams {
   GridGeom g;
   View q, k;
   double* qbar;          // [B][H][NQB][128]
-  double* kcache;        // [slots][B*H][128][NBF]
+  double* kcache;        // [slots][B*H][64][NBF][2]
   int32_t k_first;       // first KV-window frame whose K blocks are pooled
 };
 
 struct SelectParams {
   GridGeom g;
   const double* qbar;    // [B][H][NQB][128]
-  const double* kcache;  // [slots][B*H][128][NBF]
+  const double* kcache;  // [slots][B*H][64][NBF][2]
   int32_t batch;
   int32_t* row_ptr;
   int32_t* col_idx;

@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
     if (is_q)
       p.qbar[(bh * g.nqb + blk) * 128 + tid] = s;
     else
-      p.kcache[(((int64_t)tf * gridDim.z * g.heads + bh) * 128 + tid) * g.nbf + pos] = s;
+      p.kcache[((((int64_t)tf * gridDim.z * g.heads + bh) * 64 + (tid >> 1)) * g.nbf + pos) * 2 + (tid & 1)] = s;
   }
 }
 
@@ -167,8 +167,10 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
     qs[i >> 7][i & 127] = p.qbar[(bh * g.nqb + (int64_t)(tq0 + (i >> 7)) * g.nbf + pos) * 128 + (i & 127)];
   __syncthreads();
 
-  // Float64 scores.  Pooled K of key block (t, pos') sits at
-  // kcache[kv_slot[t]][bh][d][pos'].
+  // Float64 scores.  Channels d, d + 1 (d even) of the pooled K of key block
+  // (t, pos') sit together at kcache[kv_slot[t]][bh][d / 2][pos'][0..1], so
+  // a lane reads two channels per 16-byte load and neighbouring lanes
+  // (neighbouring positions) read neighbouring 16 bytes.
   if (64 * wave < w.n) {
     int64_t koff[MW];
     bool valid[MW];
@@ -180,22 +182,22 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
       valid[j] = e < w.n;
       const int kb = valid[j] ? window_kb(g, w, e) : 0;
       const int t = kb / g.nbf;
-      koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 128 * g.nbf + (kb - t * g.nbf);
+      koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 64 * g.nbf + (kb - t * g.nbf);   // in pairs
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
     }
     // more channels in flight when a lane has few candidates (latency-bound)
-#pragma unroll (MW <= 1 ? 8 : 4)
-    for (int d = 0; d < 128; ++d) {
-      const double* kd = p.kcache + (int64_t)d * g.nbf;
-      double kv[MW];
+#pragma unroll (MW <= 1 ? 4 : 2)
+    for (int dp = 0; dp < 64; ++dp) {
+      const double2* kd = reinterpret_cast<const double2*>(p.kcache) + (int64_t)dp * g.nbf;
+      double2 kv[MW];
 #pragma unroll
       for (int j = 0; j < MW; ++j) kv[j] = kd[koff[j]];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const double qd = qs[r][d];
+        const double q0 = qs[r][2 * dp], q1 = qs[r][2 * dp + 1];
 #pragma unroll
-        for (int j = 0; j < MW; ++j) acc[j][r] = fma(qd, kv[j], acc[j][r]);
+        for (int j = 0; j < MW; ++j) acc[j][r] = fma(q1, kv[j].y, fma(q0, kv[j].x, acc[j][r]));
       }
     }
 #pragma unroll
