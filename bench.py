@@ -13,9 +13,11 @@ not count), ms_per_step = select+attend ms per chunk.  roofline = the attend
 kernel (MFMA-bound) timed with HIP events on its stream; select_roofline =
 the select entry point (pool + select kernels) against HBM bandwidth;
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same
-workload.
+workload.  Means, medians and p10/p90 come from the warm steps; cold_cache
+repeats --cold-steps steps after a 512 MiB fill that evicts L2 and the
+memory-side cache before each one.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold-steps N]
   python bench.py --workload stream_768x1280 --ring   # streaming steady state
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
@@ -118,6 +120,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps timed after a 512 MiB cache flush each (0: none)")
     ap.add_argument("--ring", action="store_true",
                     help="K/V in a frame ring with the pooled-K cache: each step pools only "
                          "the chunk's q_frames new frames (streaming steady state)")
@@ -206,7 +210,28 @@ def main():
 
     sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
     att_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    both_ms = [e[0].elapsed_time(e[2]) for e in evs]
     gpu_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # Cold caches: before each of these steps a fill kernel writes 512 MiB,
+    # which evicts every XCD's L2 and the memory-side cache; the flush is
+    # outside the timed event pairs.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)
+            step(cevs[i])
+        torch.cuda.synchronize()
+        del flush
+        cold = {
+            "steps": args.cold_steps,
+            "flush_bytes": 512 << 20,
+            "select_ms_median": float(np.median([e[0].elapsed_time(e[1]) for e in cevs])),
+            "attend_ms_median": float(np.median([e[1].elapsed_time(e[2]) for e in cevs])),
+            "select_attend_ms_median": float(np.median([e[0].elapsed_time(e[2]) for e in cevs])),
+        }
     att_avg = float(np.mean(att_ms))
     sel_avg = float(np.mean(sel_ms))
     step_ms = max(wall_ms, gpu_ms)
@@ -245,6 +270,11 @@ def main():
         "attend_ms": att_avg,
         "select_ms_p10_p90": [float(np.percentile(sel_ms, 10)), float(np.percentile(sel_ms, 90))],
         "attend_ms_p10_p90": [float(np.percentile(att_ms, 10)), float(np.percentile(att_ms, 90))],
+        "select_ms_median": float(np.median(sel_ms)),
+        "attend_ms_median": float(np.median(att_ms)),
+        "select_attend_ms_median": float(np.median(both_ms)),
+        "select_attend_ms_p10_p90": [float(np.percentile(both_ms, 10)), float(np.percentile(both_ms, 90))],
+        "cold_cache": cold,
         "attend_tflops": achieved,
         "attend_frac_of_bf16_peak": achieved / PEAK_BF16_TFLOPS,
         "roofline": {
