@@ -304,13 +304,26 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
 
     // ---- S^T = K Q^T (the first step starts from a zero accumulator)
     f32x16_t s[T::kKeyTiles];
+    // K operands of step st + 1 are read while the MFMAs of step st run;
+    // scheduling barriers keep the compiler from sinking the reads back next
+    // to their MFMAs.
+    bf16x8_t ka[2][T::kKeyTiles];
+#pragma unroll
+    for (int kt = 0; kt < T::kKeyTiles; ++kt)
+      ka[0][kt] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 32 * 256 + ((half ^ ksw) & 15) * 16);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const int off = (((2 * st + half) ^ ksw) & 15) * 16;
+      if (st < 7) {
+        const int offn = (((2 * (st + 1) + half) ^ ksw) & 15) * 16;
+#pragma unroll
+        for (int kt = 0; kt < T::kKeyTiles; ++kt)
+          ka[(st + 1) & 1][kt] = *reinterpret_cast<const bf16x8_t*>(krow + kt * 32 * 256 + offn);
+      }
       dma16(vsrc, voff[st], v_lds_addr + st * T::kWaves * 1024);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kt = 0; kt < T::kKeyTiles; ++kt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + kt * 32 * 256 + off);
+        const bf16x8_t a = ka[st & 1][kt];
         if (st == 0) {
           const f32x16_t zero = {};
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0], zero, 0, 0, 0);
@@ -318,6 +331,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     const int nx = next_valid(it + 1);
     // K(nx) is issued one load per PV step below (after the V barrier, when
@@ -391,26 +405,36 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     barrier_raw();            // ... everyone's; every wave is past S, so K(it) is free
 
     // ---- O^T += V^T P^T
+    // V^T operands of PV step j + 1 are read while the MFMAs of step j run
+    // (scheduling barriers keep the order).
+    constexpr int kPvSteps = 2 * T::kKeyTiles, kPerStep = 8 / kPvSteps;
+    static_assert(kPerStep * kPvSteps == 8, "K loads spread evenly over PV steps");
+    auto vfrag = [&](int j, int dt) __attribute__((always_inline)) {
+      const int off = (((4 * dt + vchunk_lo) ^ vsw) & 15) * 16;
+      const unsigned char* base = vrow + (32 * (j >> 1) + 8 * (j & 1)) * 256 + off;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base));
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 4 * 256));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8_t va[2][4];
 #pragma unroll
-    for (int kt = 0; kt < T::kKeyTiles; ++kt)
+    for (int dt = 0; dt < 4; ++dt) va[0][dt] = vfrag(0, dt);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        // loads [j*L, j*L + L) of K(nx) at PV step j, L = 8 / steps
-        constexpr int kPvSteps = 2 * T::kKeyTiles, kPerStep = 8 / kPvSteps;
-        static_assert(kPerStep * kPvSteps == 8, "K loads spread evenly over PV steps");
+    for (int j = 0; j < kPvSteps; ++j) {
+      if (j + 1 < kPvSteps) {
 #pragma unroll
-        for (int i = (kt * 2 + s2) * kPerStep; i < (kt * 2 + s2 + 1) * kPerStep; ++i)
-          dma16(ksrc, koff[i], k_lds_addr + i * T::kWaves * 1024);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int off = (((4 * dt + vchunk_lo) ^ vsw) & 15) * 16;
-          const unsigned char* base = vrow + (32 * kt + 8 * s2) * 256 + off;
-          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base));
-          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 4 * 256));
-          const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][s2], o[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < 4; ++dt) va[(j + 1) & 1][dt] = vfrag(j + 1, dt);
       }
+      // loads [j*L, j*L + L) of K(nx) at PV step j, L = 8 / steps
+#pragma unroll
+      for (int i = j * kPerStep; i < (j + 1) * kPerStep; ++i)
+        dma16(ksrc, koff[i], k_lds_addr + i * T::kWaves * 1024);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1][dt], pb[j >> 1][j & 1], o[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     it = nx;
   }
   wait_vmcnt<0>();            // no load may still target LDS when the workgroup retires
