@@ -246,9 +246,12 @@ def test_attend_dense_special_case_equals_sdpa():
             np.testing.assert_allclose(lse[b, h], logsumexp(z, axis=1), rtol=1e-12)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_window", "small_edges", "small_16x8"])
-def test_attend_equals_token_masked_sdpa(name):
-    desc = li.CONFIGS[name]
+@pytest.mark.parametrize("name,batch", [("tiny", 1), ("tiny_window", 1), ("small_edges", 1),
+                                        ("small_16x8", 1), ("small_edges", 2)])
+def test_attend_equals_token_masked_sdpa(name, batch):
+    """Rows of the CSR follow select's (batch, head, query block) order; with
+    two batch entries a wrong row order changes the result."""
+    desc = _desc(name, batch=batch)
     g = oracle.geometry(desc)
     q, k, v = _rand_inputs(desc, 19)
     rp, ci, _ = oracle.select(g, q, k)

@@ -1,0 +1,64 @@
+"""Planted mistakes in the oracle, on the CPU: each mutant below is a copy of
+the oracle with one plausible error (a dropped term, a wrong sign, index or
+bound, a transposed or swapped operand).  The pin suite (test_oracle.py)
+must fail on every one of them, and pass on an unmodified copy, which shows
+the pins constrain each part of the oracle and that the copy is the module
+the suite imports."""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE_SRC = os.path.join(ROOT, "oracle", "lcsa_oracle.py")
+
+# (name, original text, planted text)
+MUTANTS = [
+    ("kv_frames_max", "min(qf + cf, _snap_ceil(ratio * qf))", "max(qf + cf, _snap_ceil(ratio * qf))"),
+    ("budget_floor", "return int(math.floor(x + 0.5))", "return int(math.floor(x))"),
+    ("window_half_open", "(np.abs(kx - bx) <= g.half)", "(np.abs(kx - bx) < g.half)"),
+    ("window_full_range", 'half=desc["local_range"] // 2', 'half=desc["local_range"]'),
+    ("block_tokens_transposed", "((t * g.grid_h + ys[:, None]) * g.grid_w + xs[None, :])",
+     "((t * g.grid_h + xs[None, :]) * g.grid_w + ys[:, None])"),
+    ("pool_sum_not_mean", ".sum(axis=1) / len(tok)", ".sum(axis=1)"),
+    ("score_channels_misaligned", 'kbar[:, :, e, :])', 'kbar[:, :, e, ::-1])'),
+    ("select_lowest_scores", "np.lexsort((e, -s[b, h, qb, e]))", "np.lexsort((e, s[b, h, qb, e]))"),
+    ("select_ties_to_higher", "np.lexsort((e, -s[b, h, qb, e]))", "np.lexsort((-e, -s[b, h, qb, e]))"),
+    ("select_unsorted_row", "rows.append(np.sort(order[:keep]))", "rows.append(order[:keep])"),
+    ("attend_scale_dropped", "z = (qi @ kj.T) * g.scale", "z = (qi @ kj.T)"),
+    ("attend_not_normalised", "o = (p @ vj) / den", "o = (p @ vj)"),
+    ("attend_values_are_keys", "vj = v[b, ktok, h, :]", "vj = k[b, ktok, h, :]"),
+    ("attend_lse_without_log", "lse = m[:, 0] + np.log(den[:, 0])", "lse = m[:, 0] + den[:, 0]"),
+    ("attend_row_head_swap", "r = (b * g.heads + h) * g.nqb + qb", "r = (h * g.batch + b) * g.nqb + qb"),
+    ("flops_half", "return 4.0 * g.head_dim", "return 2.0 * g.head_dim"),
+]
+
+
+def _run_suite(tmp, name, old, new):
+    d = os.path.join(tmp, name)
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    if old is not None:
+        src = open(ORACLE_SRC).read()
+        assert src.count(old) == 1, f"{name}: mutation site not unique or missing"
+        open(os.path.join(d, "oracle", "lcsa_oracle.py"), "w").write(src.replace(old, new))
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([d, ROOT]), OMP_NUM_THREADS="2")
+    # run from the copy's directory: `python -m` puts the working directory
+    # first on sys.path, so the copy shadows the repository's oracle
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle.py"),
+                        "-x", "-q", "-p", "no:cacheprovider", "--rootdir", ROOT], cwd=d, env=env,
+                       capture_output=True, text=True, timeout=900)
+    return name, r.returncode, (r.stdout + r.stderr)[-600:]
+
+
+def test_pins_fail_on_every_planted_mistake(tmp_path):
+    jobs = [("control", None, None)] + MUTANTS
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        results = list(pool.map(lambda j: _run_suite(str(tmp_path), *j), jobs))
+    control = results[0]
+    assert control[1] == 0, "unmodified oracle copy fails its pins:\n" + control[2]
+    survivors = [(n, tail) for n, rc, tail in results[1:] if rc != 1]
+    # exit status 1 = tests ran and some failed (not a collection or usage error)
+    assert not survivors, "mutants not caught by the pins: " + ", ".join(n for n, _ in survivors) \
+        + "\n" + "\n".join(t for _, t in survivors)
