@@ -296,11 +296,15 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
 
   while (it < end) {
     const int kb = col_idx[it];
+    // V(it) is issued one load per S step below, so the loads do not queue
+    // up in front of the MFMAs.  Its source address (a scalar load of the
+    // frame slot plus scalar arithmetic) is settled here, before the waits:
+    // left to the compiler it lands after the barrier, where the wait for
+    // that scalar load would also wait for the first K operand reads.
+    const char* vsrc = vbase + block_offset(kb, row_stride_v);
+    asm volatile("" : "+s"(vsrc));
     wait_vmcnt<0>();          // K(it) landed (this wave's share)
     barrier_raw();            // ... everyone's; V buffer free (PV of it-1 done)
-    // V(it) is issued one load per S step below, so the loads do not queue
-    // up in front of the MFMAs.
-    const char* vsrc = vbase + block_offset(kb, row_stride_v);
 
     // ---- S^T = K Q^T (the first step starts from a zero accumulator)
     f32x16_t s[T::kKeyTiles];
@@ -338,6 +342,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     // every wave is done with K(it)); on the last block the current block is
     // re-read instead, which keeps the loop body branch-free.
     const char* ksrc = kbase + block_offset(col_idx[nx < end ? nx : it], row_stride_k);
+    asm volatile("" : "+s"(ksrc));   // settled now, not after the PV operand reads
 
     // ---- online softmax (one query per lane, keys split over lane ^ 32)
     // P = exp2(S * scale*log2(e) - m_run) rounded to bf16 pairs; the row sum
