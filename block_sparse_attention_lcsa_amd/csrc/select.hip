@@ -187,7 +187,8 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
       for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
     }
     // more channels in flight when a lane has few candidates (latency-bound)
-#pragma unroll (MW <= 1 ? 4 : 2)
+    constexpr int kUnroll = MW <= 1 ? 4 : 2;
+#pragma unroll kUnroll
     for (int dp = 0; dp < 64; ++dp) {
       const double2* kd = reinterpret_cast<const double2*>(p.kcache) + (int64_t)dp * g.nbf;
       double2 kv[MW];
