@@ -351,6 +351,12 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     const char* ksrc = kbase + block_offset(col_idx[nx < end ? nx : it], row_stride_k);
     asm volatile("" : "+s"(ksrc));   // settled now, not after the PV operand reads
 
+    // Wave priorities: softmax 2, PV 1, S 0.  The two waves sharing a SIMD
+    // come from different workgroups and tend to fall into step (the one
+    // behind gets the MFMA pipe to itself while the other runs its softmax,
+    // and catches up), after which their VALU and MFMA phases coincide.
+    // Favouring the softmax and then PV keeps them apart.
+    __builtin_amdgcn_s_setprio(2);
     // ---- online softmax (one query per lane, keys split over lane ^ 32)
     // P = exp2(S * scale*log2(e) - m_run) rounded to bf16 pairs; the row sum
     // adds exactly these rounded values (dot with (1, 1)), one chain per key
@@ -416,6 +422,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     wait_vmcnt<0>();          // V(it) landed (the only loads in flight)
     barrier_raw();            // ... everyone's; every wave is past S, so K(it) is free
 
+    __builtin_amdgcn_s_setprio(1);
     // ---- O^T += V^T P^T
     // V^T operands of PV step j + 1 are read while the MFMAs of step j run
     // (scheduling barriers keep the order).
@@ -447,6 +454,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1][dt], pb[j >> 1][j & 1], o[dt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     it = nx;
   }
   wait_vmcnt<0>();            // no load may still target LDS when the workgroup retires
