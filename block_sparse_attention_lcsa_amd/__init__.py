@@ -151,6 +151,9 @@ class Plan:
         h = _P()
         _check(_lib.lcsa_plan_create(ctypes.byref(d), ctypes.byref(h)), "lcsa_plan_create")
         self._h = h
+        # held on the instance: module globals may already be gone when a plan
+        # is collected at interpreter exit
+        self._destroy = _lib.lcsa_plan_destroy
         self.desc = {f: getattr(d, f) for f, _ in LcsaDesc._fields_}
         inf = LcsaPlanInfo()
         _check(_lib.lcsa_plan_get_info(h, ctypes.byref(inf)), "lcsa_plan_get_info")
@@ -162,8 +165,9 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            _lib.lcsa_plan_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     @property

@@ -211,3 +211,16 @@ def test_no_device_status_on_cpu_host():
     good = _fake_view()
     assert _select(p, good, good) == 6                                # DEVICE
     assert _attend(p, good, good, good, good) == 6
+
+
+def test_plan_collected_at_interpreter_exit_is_quiet():
+    # A plan held in __main__ of a script that imported torch first is
+    # collected after the binding's globals are torn down; its destructor must
+    # not raise then.
+    code = ("import sys; sys.path.insert(0, %r); import torch; import lcsa_inputs as li; "
+            "import block_sparse_attention_lcsa_amd as lcsa; "
+            "plan = lcsa.Plan.from_desc(li.CONFIGS['tiny'])" % ROOT)
+    r = subprocess.run([os.sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "Exception ignored" not in r.stderr, r.stderr
