@@ -15,9 +15,11 @@ the select entry point (pool + select kernels) against HBM bandwidth;
 cpu_baseline = the float64 CPU oracle on a bounded sample of the same
 workload.  Means, medians and p10/p90 come from the warm steps; cold_cache
 repeats --cold-steps steps after a 512 MiB fill that evicts L2 and the
-memory-side cache before each one.
+memory-side cache before each one; graph times --graph-steps replays of
+select + attend captured once in a HIP graph.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold-steps N]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                  [--cold-steps N] [--graph-steps N]
   python bench.py --workload stream_768x1280 --ring   # streaming steady state
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
@@ -122,6 +124,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed after a 512 MiB cache flush each (0: none)")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="extra steps replayed from a HIP graph of select + attend (0: none)")
     ap.add_argument("--ring", action="store_true",
                     help="K/V in a frame ring with the pooled-K cache: each step pools only "
                          "the chunk's q_frames new frames (streaming steady state)")
@@ -232,6 +236,43 @@ def main():
             "attend_ms_median": float(np.median([e[1].elapsed_time(e[2]) for e in cevs])),
             "select_attend_ms_median": float(np.median([e[0].elapsed_time(e[2]) for e in cevs])),
         }
+    # The same select + attend captured once in a HIP graph and replayed:
+    # the step a serving loop would launch, without per-kernel launch calls.
+    graph = None
+    if args.graph_steps > 0:
+        gplan = lcsa.Plan.from_desc(desc)
+
+        def graph_body():
+            if args.ring:
+                rp, ci = lcsa.select_ring(gplan, q, k_ring, ring, new_frames, kcache, workspace=ws)
+                lcsa.attend_ring(gplan, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
+            else:
+                rp, ci = lcsa.select(gplan, q, k, workspace=ws)
+                lcsa.attend(gplan, q, k, v, rp, ci, out=out, workspace=att_ws)
+            return rp, ci
+
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            graph_body()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            g_out = graph_body()
+        for _ in range(3):
+            g.replay()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        gev[0].record(stream)
+        for _ in range(args.graph_steps):
+            g.replay()
+        gev[1].record(stream)
+        torch.cuda.synchronize()
+        graph = {"steps": args.graph_steps,
+                 "select_attend_ms": gev[0].elapsed_time(gev[1]) / args.graph_steps}
+        del g, g_out
+
     att_avg = float(np.mean(att_ms))
     sel_avg = float(np.mean(sel_ms))
     step_ms = max(wall_ms, gpu_ms)
@@ -275,6 +316,7 @@ def main():
         "select_attend_ms_median": float(np.median(both_ms)),
         "select_attend_ms_p10_p90": [float(np.percentile(both_ms, 10)), float(np.percentile(both_ms, 90))],
         "cold_cache": cold,
+        "graph": graph,
         "attend_tflops": achieved,
         "attend_frac_of_bf16_peak": achieved / PEAK_BF16_TFLOPS,
         "roofline": {
