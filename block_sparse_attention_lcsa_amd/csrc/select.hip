@@ -186,19 +186,45 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
     }
-    // more channels in flight when a lane has few candidates (latency-bound)
-    constexpr int kUnroll = MW <= 1 ? 4 : 2;
-#pragma unroll kUnroll
-    for (int dp = 0; dp < 64; ++dp) {
-      const double2* kd = reinterpret_cast<const double2*>(p.kcache) + (int64_t)dp * g.nbf;
-      double2 kv[MW];
+    const double2* kd = reinterpret_cast<const double2*>(p.kcache);
+    if constexpr (MW == 1) {
+      // One candidate per lane: latency-bound.  Channel pairs go in steps of
+      // kU, and the loads of step i + 1 are issued before the FMAs of step i,
+      // so a load latency overlaps a step of arithmetic (same FMA order).
+      constexpr int kU = 4;
+      double2 cur[kU], nxt[kU];
 #pragma unroll
-      for (int j = 0; j < MW; ++j) kv[j] = kd[koff[j]];
+      for (int u = 0; u < kU; ++u) cur[u] = kd[(int64_t)u * g.nbf + koff[0]];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const double q0 = qs[r][2 * dp], q1 = qs[r][2 * dp + 1];
+      for (int dp0 = 0; dp0 < 64; dp0 += kU) {
+        if (dp0 + kU < 64) {
 #pragma unroll
-        for (int j = 0; j < MW; ++j) acc[j][r] = fma(q1, kv[j].y, fma(q0, kv[j].x, acc[j][r]));
+          for (int u = 0; u < kU; ++u) nxt[u] = kd[(int64_t)(dp0 + kU + u) * g.nbf + koff[0]];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int dp = dp0 + u;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const double q0 = qs[r][2 * dp], q1 = qs[r][2 * dp + 1];
+            acc[0][r] = fma(q1, cur[u].y, fma(q0, cur[u].x, acc[0][r]));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
+      }
+    } else {
+#pragma unroll 2
+      for (int dp = 0; dp < 64; ++dp) {
+        double2 kv[MW];
+#pragma unroll
+        for (int j = 0; j < MW; ++j) kv[j] = kd[(int64_t)dp * g.nbf + koff[j]];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const double q0 = qs[r][2 * dp], q1 = qs[r][2 * dp + 1];
+#pragma unroll
+          for (int j = 0; j < MW; ++j) acc[j][r] = fma(q1, kv[j].y, fma(q0, kv[j].x, acc[j][r]));
+        }
       }
     }
 #pragma unroll
