@@ -260,7 +260,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             g_out = graph_body()
-        for _ in range(3):
+        for _ in range(10):      # the first replays of a new graph run slower
             g.replay()
         gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()

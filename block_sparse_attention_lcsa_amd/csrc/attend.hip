@@ -505,7 +505,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
 // 16 y + 15; thread t handles query 16 y + t / 16 and channels 8 (t % 16) ..
 // +7, so 16 lanes read one query's 512-byte partial row.  Pieces hold O and
 // the row sum against their own reference m (log2 units); the merge rescales
-// each to the largest m.  A row whose pieces hold no valid block gives O = 0,
+// them to a running maximum, four pieces at a time.  A row whose pieces hold no valid block gives O = 0,
 // LSE = -inf.
 constexpr int kMergeThreads = 256;
 template <int BT>
@@ -524,27 +524,51 @@ __global__ void __launch_bounds__(kMergeThreads) attend_merge_kernel(AttendParam
   const int64_t items = (p.rows - p.full_rows) * p.pieces;
   const float* ml = p.part + items * BT * 128;
 
-  float m = -__builtin_huge_valf();
-  for (int pc = 0; pc < p.pieces; ++pc) m = fmaxf(m, ml[((tr * p.pieces + pc) * BT + qi) * 2]);
+  // Pieces in groups of four: all loads of a group are issued before any
+  // use, and groups fold into a running (m, l, acc) with one rescale each.
+  constexpr int kG = 4;
+  float m = -__builtin_huge_valf(), l = 0.0f;
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-  float l = 0.0f;
-  if (m > -__builtin_huge_valf()) {
-    for (int pc = 0; pc < p.pieces; ++pc) {
-      const int64_t it = tr * p.pieces + pc;
-      const float2 mlp = *reinterpret_cast<const float2*>(ml + (it * BT + qi) * 2);
-      const float w = __builtin_amdgcn_exp2f(mlp.x - m);   // 0 for an empty piece
-      l = fmaf(w, mlp.y, l);
-      const float4* src = reinterpret_cast<const float4*>(p.part + (it * BT + qi) * 128 + c0);
+  for (int pc0 = 0; pc0 < p.pieces; pc0 += kG) {
+    const int np = min(kG, p.pieces - pc0);
+    float2 mlp[kG];
+    float4 x[kG][2];
 #pragma unroll
-      for (int c4 = 0; c4 < 2; ++c4) {
-        const float4 x = src[c4];
-        acc[4 * c4 + 0] = fmaf(w, x.x, acc[4 * c4 + 0]);
-        acc[4 * c4 + 1] = fmaf(w, x.y, acc[4 * c4 + 1]);
-        acc[4 * c4 + 2] = fmaf(w, x.z, acc[4 * c4 + 2]);
-        acc[4 * c4 + 3] = fmaf(w, x.w, acc[4 * c4 + 3]);
+    for (int u = 0; u < kG; ++u) {
+      if (u < np) {
+        const int64_t it = tr * p.pieces + pc0 + u;
+        mlp[u] = *reinterpret_cast<const float2*>(ml + (it * BT + qi) * 2);
+        const float4* src = reinterpret_cast<const float4*>(p.part + (it * BT + qi) * 128 + c0);
+        x[u][0] = src[0];
+        x[u][1] = src[1];
       }
+    }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < kG; ++u)
+      if (u < np) mc = fmaxf(mc, mlp[u].x);
+    if (mc > -__builtin_huge_valf()) {
+      const float sc = __builtin_amdgcn_exp2f(m - mc);   // 0 while nothing was held
+      l *= sc;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] *= sc;
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        if (u < np) {
+          const float w = __builtin_amdgcn_exp2f(mlp[u].x - mc);   // 0 for an empty piece
+          l = fmaf(w, mlp[u].y, l);
+#pragma unroll
+          for (int c4 = 0; c4 < 2; ++c4) {
+            acc[4 * c4 + 0] = fmaf(w, x[u][c4].x, acc[4 * c4 + 0]);
+            acc[4 * c4 + 1] = fmaf(w, x[u][c4].y, acc[4 * c4 + 1]);
+            acc[4 * c4 + 2] = fmaf(w, x[u][c4].z, acc[4 * c4 + 2]);
+            acc[4 * c4 + 3] = fmaf(w, x[u][c4].w, acc[4 * c4 + 3]);
+          }
+        }
+      }
+      m = mc;
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
