@@ -2,7 +2,8 @@
 
 This module is shared by the oracle, the tests and the bench.  It holds no
 step of the attention method itself: only workload descriptors, the seeded
-generator of Q/K/V and bf16 bit conversions.
+generator of Q/K/V, synthetic rotary-embedding tables (inputs a caller
+supplies) and bf16 bit conversions.
 
 Workloads (token grids are the latent grid after the DiT's 2x2 patching, so
 a H x W output video gives a (H/16) x (W/16) token grid):
@@ -168,3 +169,23 @@ def generate(desc: dict, seed: int = 0) -> Inputs:
     for name in ("q", "k", "v"):
         h.update(out[name].tobytes())
     return Inputs(q=out["q"], k=out["k"], v=out["v"], kv_frames=kvf, sha256=h.hexdigest())
+
+
+# ------------------------------------------------------------ RoPE tables
+def rope_tables(desc: dict, pairs=(22, 21, 21), base: float = 10000.0, frame_offset: int = 0):
+    """Synthetic cos/sin tables of a factored 3D rotary embedding, as a caller
+    would supply them: for axis a with n pairs, pair j turns by
+    pos * base**(-j / n) radians at axis position pos (the frame index is
+    frame_offset + window frame).  Returns float32 arrays t [kv_frames, pt, 2],
+    h [grid_h, ph, 2], w [grid_w, pw, 2] of (cos, sin).  The 22/21/21 split
+    of head_dim 128 gives the spare pair to the time axis."""
+    kvf = kv_frames_of(desc)
+
+    def table(positions, n):
+        ang = np.asarray(positions, dtype=np.float64)[:, None] * base ** (-np.arange(n) / n)[None, :]
+        return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+    pt, ph, pw = pairs
+    return {"t": table(frame_offset + np.arange(kvf), pt),
+            "h": table(np.arange(desc["grid_h"]), ph),
+            "w": table(np.arange(desc["grid_w"]), pw)}

@@ -2,3 +2,4 @@
 the smoke check and the bench's CPU-baseline leg use it; the library never
 does."""
 from .lcsa_oracle import *  # noqa: F401,F403
+from .rope_oracle import *  # noqa: F401,F403

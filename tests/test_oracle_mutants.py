@@ -1,9 +1,9 @@
 """Planted mistakes in the oracle, on the CPU: each mutant below is a copy of
 the oracle with one plausible error (a dropped term, a wrong sign, index or
-bound, a transposed or swapped operand).  The pin suite (test_oracle.py)
-must fail on every one of them, and pass on an unmodified copy, which shows
-the pins constrain each part of the oracle and that the copy is the module
-the suite imports."""
+bound, a transposed or swapped operand).  The pin suites (test_oracle.py,
+test_oracle_rope.py) must fail on every one of them, and pass on an
+unmodified copy, which shows the pins constrain each part of the oracle and
+that the copy is the module the suites import."""
 import os
 import shutil
 import subprocess
@@ -11,9 +11,10 @@ import sys
 from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-ORACLE_SRC = os.path.join(ROOT, "oracle", "lcsa_oracle.py")
+PIN_SUITES = [os.path.join(ROOT, "tests", "test_oracle.py"),
+              os.path.join(ROOT, "tests", "test_oracle_rope.py")]
 
-# (name, original text, planted text)
+# (name, original text, planted text) in oracle/lcsa_oracle.py
 MUTANTS = [
     ("kv_frames_max", "min(qf + cf, _snap_ceil(ratio * qf))", "max(qf + cf, _snap_ceil(ratio * qf))"),
     ("budget_floor", "return int(math.floor(x + 0.5))", "return int(math.floor(x))"),
@@ -34,27 +35,40 @@ MUTANTS = [
     ("flops_half", "return 4.0 * g.head_dim", "return 2.0 * g.head_dim"),
 ]
 
+# the same in oracle/rope_oracle.py
+ROPE_MUTANTS = [
+    ("rope_sine_sign", "out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s"),
+    ("rope_rows_and_columns_swapped", "tab.h[pos_h], tab.w[pos_w]", "tab.h[pos_w % tab.h.shape[0]], tab.w[pos_h]"),
+    ("rope_query_frame_offset", "g.kv_frames - g.q_frames, round_out", "0, round_out"),
+    ("rope_rounds_through_float32", "b = np.ascontiguousarray(x, dtype=np.float64)",
+     "b = np.ascontiguousarray(np.asarray(x, dtype=np.float32), dtype=np.float64)"),
+    ("rope_ties_away_from_zero", "(b + half_minus_one + lsb)", "(b + half_minus_one + np.uint64(1))"),
+    ("rope_token_row_from_columns", "(s // grid_w) % grid_h, s % grid_w", "s % grid_h, s % grid_w"),
+]
 
-def _run_suite(tmp, name, old, new):
+
+def _run_suite(tmp, name, fname, old, new):
     d = os.path.join(tmp, name)
     shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
                     ignore=shutil.ignore_patterns("__pycache__"))
     if old is not None:
-        src = open(ORACLE_SRC).read()
+        src = open(os.path.join(ROOT, "oracle", fname)).read()
         assert src.count(old) == 1, f"{name}: mutation site not unique or missing"
-        open(os.path.join(d, "oracle", "lcsa_oracle.py"), "w").write(src.replace(old, new))
+        open(os.path.join(d, "oracle", fname), "w").write(src.replace(old, new))
     env = dict(os.environ, PYTHONPATH=os.pathsep.join([d, ROOT]), OMP_NUM_THREADS="2")
     # run from the copy's directory: `python -m` puts the working directory
     # first on sys.path, so the copy shadows the repository's oracle
-    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle.py"),
+    r = subprocess.run([sys.executable, "-m", "pytest", *PIN_SUITES,
                         "-x", "-q", "-p", "no:cacheprovider", "--rootdir", ROOT], cwd=d, env=env,
                        capture_output=True, text=True, timeout=900)
     return name, r.returncode, (r.stdout + r.stderr)[-600:]
 
 
 def test_pins_fail_on_every_planted_mistake(tmp_path):
-    jobs = [("control", None, None)] + MUTANTS
-    with ThreadPoolExecutor(max_workers=4) as pool:
+    jobs = ([("control", None, None, None)]
+            + [(n, "lcsa_oracle.py", a, b) for n, a, b in MUTANTS]
+            + [(n, "rope_oracle.py", a, b) for n, a, b in ROPE_MUTANTS])
+    with ThreadPoolExecutor(max_workers=6) as pool:
         results = list(pool.map(lambda j: _run_suite(str(tmp_path), *j), jobs))
     control = results[0]
     assert control[1] == 0, "unmodified oracle copy fails its pins:\n" + control[2]
