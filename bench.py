@@ -21,6 +21,7 @@ select + attend captured once in a HIP graph.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                   [--cold-steps N] [--graph-steps N]
   python bench.py --workload stream_768x1280 --ring   # streaming steady state
+  python bench.py --rope                               # rotary embedding fused into select
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -58,8 +59,9 @@ def _traffic(workload):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(name, desc, inp, useful_flops):
-    """Time the oracle as it stands on a bounded sample and scale to a step."""
+def cpu_baseline(name, desc, inp, useful_flops, rope_tables=None):
+    """Time the oracle as it stands on a bounded sample and scale to a step
+    (with rope_tables, the oracle's rotary embedding of Q and K first)."""
     import numpy as np
     import lcsa_inputs as li
     import oracle
@@ -71,6 +73,9 @@ def cpu_baseline(name, desc, inp, useful_flops):
     g = oracle.geometry(desc)
     qf, kf, vf = (li.bf16_bits_to_f32(x) for x in (inp.q, inp.k, inp.v))
     t0 = time.perf_counter()
+    if rope_tables is not None:
+        tab = oracle.RopeTables(t=rope_tables["t"], h=rope_tables["h"], w=rope_tables["w"])
+        qf, kf = oracle.rope_q(g, qf, tab), oracle.rope_k(g, kf, tab)
     rp, ci, _ = oracle.select(g, qf, kf)
     t_sel = time.perf_counter() - t0
     rows = len(rp) - 1
@@ -93,7 +98,8 @@ def cpu_baseline(name, desc, inp, useful_flops):
         "cores": int(blas_threads),
         "kind": "oracle",
         "ms_per_step": step_s * 1e3,
-        "sample": (f"{name}: oracle select on all {rows} CSR rows ({t_sel:.2f} s) + oracle "
+        "sample": (f"{name}: oracle {'rotary embedding + ' if rope_tables is not None else ''}"
+                   f"select on all {rows} CSR rows ({t_sel:.2f} s) + oracle "
                    f"attention on {done} of {rows} rows ({t_att:.2f} s), scaled to the full "
                    f"step; float64 numpy, {blas_threads} BLAS threads, "
                    f"{len(os.sched_getaffinity(0))} host cores visible"),
@@ -126,6 +132,9 @@ def main():
                     help="extra steps timed after a 512 MiB cache flush each (0: none)")
     ap.add_argument("--graph-steps", type=int, default=20,
                     help="extra steps replayed from a HIP graph of select + attend (0: none)")
+    ap.add_argument("--rope", action="store_true",
+                    help="factored 3D rotary embedding fused into select (lcsa_select_rope): "
+                         "the step turns Q and K, pools the turned values and attends on them")
     ap.add_argument("--ring", action="store_true",
                     help="K/V in a frame ring with the pooled-K cache: each step pools only "
                          "the chunk's q_frames new frames (streaming steady state)")
@@ -163,6 +172,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     new_frames = info["kv_frames"]
+    if args.rope and args.ring:
+        print("bench.py: --rope and --ring together are not timed here", file=sys.stderr)
+        sys.exit(2)
+    if args.rope:
+        tabs = li.rope_tables(desc)
+        rtab = lcsa.rope(*(torch.from_numpy(tabs[a]).to(dev) for a in ("t", "h", "w")))
+        q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
     if args.ring:
         # ring of kv_frames slots, window frame t in slot (t + 1) % slots;
         # the cache is filled once, then each step pools the newest q_frames
@@ -185,12 +201,16 @@ def main():
             ev[0].record(stream)
         if args.ring:
             rp, ci = lcsa.select_ring(p, q, k_ring, ring, new_frames, kcache, workspace=ws)
+        elif args.rope:
+            _, _, rp, ci = lcsa.select_rope(p, q, k, rtab, q_rot=q_rot, k_rot=k_rot, workspace=ws)
         else:
             rp, ci = lcsa.select(p, q, k, workspace=ws)
         if ev:
             ev[1].record(stream)
         if args.ring:
             lcsa.attend_ring(p, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
+        elif args.rope:
+            lcsa.attend(p, q_rot, k_rot, v, rp, ci, out=out, workspace=att_ws)
         else:
             lcsa.attend(p, q, k, v, rp, ci, out=out, workspace=att_ws)
         if ev:
@@ -246,6 +266,10 @@ def main():
             if args.ring:
                 rp, ci = lcsa.select_ring(gplan, q, k_ring, ring, new_frames, kcache, workspace=ws)
                 lcsa.attend_ring(gplan, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
+            elif args.rope:
+                _, _, rp, ci = lcsa.select_rope(gplan, q, k, rtab, q_rot=q_rot, k_rot=k_rot,
+                                                workspace=ws)
+                lcsa.attend(gplan, q_rot, k_rot, v, rp, ci, out=out, workspace=att_ws)
             else:
                 rp, ci = lcsa.select(gplan, q, k, workspace=ws)
                 lcsa.attend(gplan, q, k, v, rp, ci, out=out, workspace=att_ws)
@@ -273,6 +297,36 @@ def main():
                  "select_attend_ms": gev[0].elapsed_time(gev[1]) / args.graph_steps}
         del g, g_out
 
+    # Rotary embedding: the fused select against plain select on the same
+    # inputs plus a device copy of Q and K, the least a separate rotary pass
+    # (read Q and K, write the turned tensors) would cost.
+    rope_cmp = None
+    if args.rope:
+        def tmed(fn, n=20):
+            ts = []
+            for _ in range(n):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in ts]))
+        rope_plan = lcsa.Plan.from_desc(desc)
+        for _ in range(3):
+            lcsa.select(rope_plan, q, k, workspace=ws)
+        plain_ms = tmed(lambda: lcsa.select(rope_plan, q, k, workspace=ws))
+        fused_ms = tmed(lambda: lcsa.select_rope(rope_plan, q, k, rtab, q_rot=q_rot, k_rot=k_rot,
+                                                 workspace=ws))
+
+        def copy_qk():
+            q_rot.copy_(q)
+            k_rot.copy_(k)
+        copy_ms = tmed(copy_qk)
+        rope_cmp = {"select_rope_ms_median": fused_ms, "select_ms_median_without_rope": plain_ms,
+                    "qk_copy_ms_median": copy_ms,
+                    "separate_pass_lower_bound_ms": plain_ms + copy_ms}
+
     att_avg = float(np.mean(att_ms))
     sel_avg = float(np.mean(sel_ms))
     step_ms = max(wall_ms, gpu_ms)
@@ -280,8 +334,9 @@ def main():
     # select: algorithmic HBM bytes = Q and K read once (bf16) + the CSR
     # written (row_ptr and col_idx, int32)
     pooled_kv_tokens = info["kv_tokens"] * new_frames // info["kv_frames"]
-    sel_bytes = (2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + pooled_kv_tokens)
-                 + 4 * (info["rows"] + 1 + info["nnz"]))
+    qk_bytes = 2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + pooled_kv_tokens)
+    # with the rotary embedding the turned Q and K are written as well
+    sel_bytes = qk_bytes * (2 if args.rope else 1) + 4 * (info["rows"] + 1 + info["nnz"])
     sel_gbs = sel_bytes / (sel_avg * 1e-3) / 1e9
 
     res = {
@@ -305,6 +360,7 @@ def main():
             "k": info["k"], "selected_pairs": info["nnz"], "useful_tflop": flops / 1e12,
             "seed": args.seed, "inputs_sha256": inp.sha256,
             "kv_storage": "frame ring + pooled-K cache" if args.ring else "contiguous window",
+            "rope": "factored 3D, fused into select (22/21/21 pairs)" if args.rope else None,
             "pooled_kv_frames": new_frames,
         },
         "select_ms": sel_avg,
@@ -317,6 +373,7 @@ def main():
         "select_attend_ms_p10_p90": [float(np.percentile(both_ms, 10)), float(np.percentile(both_ms, 90))],
         "cold_cache": cold,
         "graph": graph,
+        "rope_fusion": rope_cmp,
         "attend_tflops": achieved,
         "attend_frac_of_bf16_peak": achieved / PEAK_BF16_TFLOPS,
         "roofline": {
@@ -338,7 +395,7 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(name, desc, inp, flops)
+        res["cpu_baseline"] = cpu_baseline(name, desc, inp, flops, tabs if args.rope else None)
     print(json.dumps(res), flush=True)
 
 

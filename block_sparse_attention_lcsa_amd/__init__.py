@@ -18,8 +18,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "LcsaError", "select", "attend", "select_ring", "attend_ring", "lib_path",
-           "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
+__all__ = ["Plan", "LcsaError", "select", "attend", "select_ring", "attend_ring", "select_rope",
+           "select_ring_rope", "rope", "lib_path", "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -38,7 +38,8 @@ _lib = ctypes.CDLL(lib_path())
 # Every symbol include/lcsa.h declares.
 EXPORTS = [
     "lcsa_plan_create", "lcsa_plan_destroy", "lcsa_plan_get_info", "lcsa_plan_row_ptr",
-    "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_select_ring", "lcsa_attend_ring",
+    "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_select_rope",
+    "lcsa_select_ring_rope", "lcsa_select_ring", "lcsa_attend_ring",
     "lcsa_status_string", "lcsa_last_error", "lcsa_abi_version",
 ]
 MAX_KV_FRAMES = 64
@@ -68,6 +69,13 @@ class LcsaTensor(ctypes.Structure):
 
 class LcsaKvRing(ctypes.Structure):
     _fields_ = [("slots", ctypes.c_int32), ("frame_slot", ctypes.c_int32 * 64)]
+
+
+class LcsaRope(ctypes.Structure):
+    _fields_ = [("pairs_t", ctypes.c_int32), ("pairs_h", ctypes.c_int32),
+                ("pairs_w", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("table_t", ctypes.c_void_p), ("table_h", ctypes.c_void_p),
+                ("table_w", ctypes.c_void_p)]
 
 
 class LcsaPlanInfo(ctypes.Structure):
@@ -108,6 +116,16 @@ _lib.lcsa_select_ring.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER
                                   ctypes.POINTER(LcsaKvRing), ctypes.c_int32, _P,
                                   _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.lcsa_select_ring.restype = ctypes.c_int32
+_lib.lcsa_select_rope.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                  ctypes.POINTER(LcsaRope), ctypes.POINTER(LcsaTensor),
+                                  ctypes.POINTER(LcsaTensor), _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lcsa_select_rope.restype = ctypes.c_int32
+_lib.lcsa_select_ring_rope.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                       ctypes.POINTER(LcsaKvRing), ctypes.c_int32, _P,
+                                       ctypes.POINTER(LcsaRope), ctypes.POINTER(LcsaTensor),
+                                       ctypes.POINTER(LcsaTensor), _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]
+_lib.lcsa_select_ring_rope.restype = ctypes.c_int32
 _lib.lcsa_attend_ring.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
                                   ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaKvRing), _P, _P,
                                   ctypes.c_int64, ctypes.POINTER(LcsaTensor), _P, _P,
@@ -397,3 +415,105 @@ def attend_ring(plan: Plan, q, k_ring, v_ring, ring: LcsaKvRing, row_ptr, col_id
     if return_lse:
         return out, lse
     return out
+
+
+def rope(table_t, table_h, table_w) -> "RopeTables":
+    """Rotary tables for select_rope / select_ring_rope: float32 device
+    tensors [kv_frames, pairs_t, 2], [grid_h, pairs_h, 2], [grid_w, pairs_w, 2]
+    of (cos, sin); pairs_t + pairs_h + pairs_w = 64."""
+    return RopeTables(table_t, table_h, table_w)
+
+
+class RopeTables:
+    def __init__(self, table_t, table_h, table_w):
+        import torch
+        tabs = (table_t, table_h, table_w)
+        for t in tabs:
+            if t.dtype != torch.float32 or t.dim() != 3 or t.shape[2] != 2 or not t.is_contiguous():
+                raise ValueError("rotary tables must be contiguous float32 [positions, pairs, 2]")
+            if not t.is_cuda:
+                raise ValueError("rotary tables must be device tensors")
+        self.tables = tabs
+        self.desc = LcsaRope(pairs_t=table_t.shape[1], pairs_h=table_h.shape[1],
+                             pairs_w=table_w.shape[1], reserved=0,
+                             table_t=table_t.data_ptr() if table_t.numel() else None,
+                             table_h=table_h.data_ptr() if table_h.numel() else None,
+                             table_w=table_w.data_ptr() if table_w.numel() else None)
+
+    def check(self, plan: Plan):
+        d, inf = plan.desc, plan.info
+        want = ((inf["kv_frames"],), (d["grid_h"],), (d["grid_w"],))
+        for t, w in zip(self.tables, want):
+            if t.numel() and t.shape[0] != w[0]:
+                raise ValueError(f"rotary table of {t.shape[0]} positions, plan needs {w[0]}")
+
+
+def select_rope(plan: Plan, q, k, tables: "RopeTables", q_rot=None, k_rot=None,
+                return_scores: bool = False, workspace=None, stream=None):
+    """Rotary embedding fused into selection: returns (q_rot, k_rot, row_ptr,
+    col_idx[, scores]) where q_rot / k_rot are the turned bf16 Q and K
+    (written into the given tensors if passed, which may be q and k) and the
+    CSR is selected on them.  Pass q_rot, k_rot to attend."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_shape(k, plan, "kv_tokens", "k")
+    tables.check(plan)
+    q_rot = torch.empty_like(q, memory_format=torch.contiguous_format) if q_rot is None else q_rot
+    k_rot = torch.empty_like(k, memory_format=torch.contiguous_format) if k_rot is None else k_rot
+    _check_shape(q_rot, plan, "q_tokens", "q_rot")
+    _check_shape(k_rot, plan, "kv_tokens", "k_rot")
+    inf = plan.info
+    dev = q.device
+    row_ptr = torch.empty(inf["rows"] + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(inf["nnz"], 1), dtype=torch.int32, device=dev)[: inf["nnz"]]
+    if workspace is None:
+        workspace = torch.empty(max(int(inf["select_workspace_bytes"]), 256), dtype=torch.uint8,
+                                device=dev)
+    scores = None
+    if return_scores:
+        d = plan.desc
+        scores = torch.empty((d["batch"], d["heads"], inf["nqb"], inf["nkb"]),
+                             dtype=torch.float64, device=dev)
+    qv, kv, qr, kr = tensor_view(q), tensor_view(k), tensor_view(q_rot), tensor_view(k_rot)
+    st = _lib.lcsa_select_rope(plan.handle, ctypes.byref(qv), ctypes.byref(kv),
+                               ctypes.byref(tables.desc), ctypes.byref(qr), ctypes.byref(kr),
+                               row_ptr.data_ptr(), col_idx.data_ptr() if inf["nnz"] else None,
+                               scores.data_ptr() if scores is not None else None,
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream_ptr(q, stream))
+    _check(st, "lcsa_select_rope")
+    out = (q_rot, k_rot, row_ptr, col_idx)
+    return out + (scores,) if return_scores else out
+
+
+def select_ring_rope(plan: Plan, q, k_ring, ring: LcsaKvRing, new_frames: int, kcache,
+                     tables: "RopeTables", k_rot_ring, q_rot=None, workspace=None, stream=None):
+    """select_ring with the rotary embedding: the newest new_frames window
+    frames of k_ring are turned into the same slots of k_rot_ring and pooled
+    into kcache; Q is turned into q_rot.  Returns (q_rot, row_ptr, col_idx)."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_ring_tensor(k_ring, plan, ring.slots, "k_ring")
+    _check_ring_tensor(k_rot_ring, plan, ring.slots, "k_rot_ring")
+    tables.check(plan)
+    if kcache.dtype != torch.float64 or kcache.numel() * 8 < kcache_bytes(plan, ring.slots):
+        raise ValueError("kcache must be float64 with kcache_bytes(plan, slots) bytes")
+    q_rot = torch.empty_like(q, memory_format=torch.contiguous_format) if q_rot is None else q_rot
+    _check_shape(q_rot, plan, "q_tokens", "q_rot")
+    inf = plan.info
+    dev = q.device
+    row_ptr = torch.empty(inf["rows"] + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(inf["nnz"], 1), dtype=torch.int32, device=dev)[: inf["nnz"]]
+    if workspace is None:
+        workspace = torch.empty(max(int(inf["select_workspace_bytes"]), 256), dtype=torch.uint8,
+                                device=dev)
+    qv, kv, qr, kr = tensor_view(q), tensor_view(k_ring), tensor_view(q_rot), tensor_view(k_rot_ring)
+    st = _lib.lcsa_select_ring_rope(plan.handle, ctypes.byref(qv), ctypes.byref(kv),
+                                    ctypes.byref(ring), int(new_frames), kcache.data_ptr(),
+                                    ctypes.byref(tables.desc), ctypes.byref(qr), ctypes.byref(kr),
+                                    row_ptr.data_ptr(), col_idx.data_ptr() if inf["nnz"] else None,
+                                    None, workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream_ptr(q, stream))
+    _check(st, "lcsa_select_ring_rope")
+    return q_rot, row_ptr, col_idx

@@ -133,16 +133,39 @@ View make_view(const lcsa_tensor* t) {
 // Shared body of lcsa_select (ring == NULL: K is the contiguous window, the
 // pooled K of every window frame goes to the workspace) and lcsa_select_ring
 // (the newest new_frames frames are pooled into the caller's cache).
+// Rotary tables and the rotated Q / K outputs of lcsa_select_rope and
+// lcsa_select_ring_rope.
+lcsa_status check_rope(const char* fn, const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                       const lcsa_tensor* k_rot) {
+  if (!rope) return fail(LCSA_ERR_NULL, "%s: rope is NULL", fn);
+  const int pt = rope->pairs_t, ph = rope->pairs_h, pw = rope->pairs_w;
+  if (pt < 0 || ph < 0 || pw < 0 || pt + ph + pw != kHeadDim / 2 || rope->reserved != 0)
+    return fail(LCSA_ERR_INVALID, "%s: rotary pairs %d + %d + %d must be %d (reserved 0)", fn,
+                pt, ph, pw, kHeadDim / 2);
+  if ((pt > 0 && !rope->table_t) || (ph > 0 && !rope->table_h) || (pw > 0 && !rope->table_w))
+    return fail(LCSA_ERR_NULL, "%s: a rotary table with pairs is NULL", fn);
+  const float* tabs[3] = {rope->table_t, rope->table_h, rope->table_w};
+  for (const float* tb : tabs)
+    if (reinterpret_cast<uintptr_t>(tb) % 8)
+      return fail(LCSA_ERR_ALIGN, "%s: rotary tables must be 8-byte aligned", fn);
+  lcsa_status st;
+  if ((st = check_view("q_rot", q_rot, 0, 0))) return st;
+  if ((st = check_view("k_rot", k_rot, 0, 0))) return st;
+  return LCSA_OK;
+}
+
 lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tensor* q,
                         const lcsa_tensor* k, const lcsa_kv_ring* ring, int new_frames,
                         double* d_kcache, int32_t* d_row_ptr, int32_t* d_col_idx,
                         double* d_scores, void* d_workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, const lcsa_rope* rope = nullptr,
+                        const lcsa_tensor* q_rot = nullptr, const lcsa_tensor* k_rot = nullptr) {
   if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
   if ((st = check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
   if ((st = check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
+  if (rope && (st = check_rope(fn, rope, q_rot, k_rot))) return st;
   if (!d_row_ptr || !d_col_idx) return fail(LCSA_ERR_NULL, "%s: CSR buffers are NULL", fn);
   if (in.max_window > kMaxWindow)
     return fail(LCSA_ERR_SHAPE, "window of %d key blocks exceeds the select limit of %d",
@@ -165,7 +188,19 @@ lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   pp.kcache = ring ? d_kcache
                    : reinterpret_cast<double*>(static_cast<char*>(d_workspace) + qbar_bytes);
   pp.k_first = ring ? in.kv_frames - new_frames : 0;
-  hipError_t e = launch_pool(pp, plan->desc.batch, in.block_tokens, s);
+  pp.rope = RopeParams{};
+  if (rope) {
+    pp.rope.table_t = rope->table_t;
+    pp.rope.table_h = rope->table_h;
+    pp.rope.table_w = rope->table_w;
+    pp.rope.pt = rope->pairs_t;
+    pp.rope.ph = rope->pairs_h;
+    pp.rope.q_rot = OutView{static_cast<uint16_t*>(q_rot->data), q_rot->stride_b, q_rot->stride_s,
+                            q_rot->stride_h};
+    pp.rope.k_rot = OutView{static_cast<uint16_t*>(k_rot->data), k_rot->stride_b, k_rot->stride_s,
+                            k_rot->stride_h};
+  }
+  hipError_t e = launch_pool(pp, plan->desc.batch, in.block_tokens, rope != nullptr, s);
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "pool launch: %s", hipGetErrorString(e));
 
   SelectParams sp;
@@ -289,6 +324,40 @@ lcsa_status lcsa_select_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_
     return fail(LCSA_ERR_ALIGN, "lcsa_select_ring: pooled-K cache not 256-byte aligned");
   return lcsa::select_impl("lcsa_select_ring", plan, q, k_ring, ring, new_frames, d_kcache,
                            d_row_ptr, d_col_idx, d_scores, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_select_rope(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                             const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                             const lcsa_tensor* k_rot, int32_t* d_row_ptr, int32_t* d_col_idx,
+                             double* d_scores, void* d_workspace, size_t workspace_bytes,
+                             void* stream) {
+  lcsa::clear_error();
+  if (!rope) return fail(LCSA_ERR_NULL, "lcsa_select_rope: rope is NULL");
+  return lcsa::select_impl("lcsa_select_rope", plan, q, k, nullptr, 0, nullptr, d_row_ptr,
+                           d_col_idx, d_scores, d_workspace, workspace_bytes, stream, rope, q_rot,
+                           k_rot);
+}
+
+lcsa_status lcsa_select_ring_rope(lcsa_plan_t plan, const lcsa_tensor* q,
+                                  const lcsa_tensor* k_ring, const lcsa_kv_ring* ring,
+                                  int32_t new_frames, double* d_kcache, const lcsa_rope* rope,
+                                  const lcsa_tensor* q_rot, const lcsa_tensor* k_rot_ring,
+                                  int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                                  void* d_workspace, size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_select_ring_rope: plan is NULL");
+  if (!rope) return fail(LCSA_ERR_NULL, "lcsa_select_ring_rope: rope is NULL");
+  lcsa_status st;
+  if ((st = lcsa::check_ring("lcsa_select_ring_rope", plan, ring))) return st;
+  if (new_frames < 0 || new_frames > plan->info.kv_frames)
+    return fail(LCSA_ERR_INVALID, "lcsa_select_ring_rope: new_frames %d outside [0, %d]",
+                new_frames, plan->info.kv_frames);
+  if (!d_kcache) return fail(LCSA_ERR_NULL, "lcsa_select_ring_rope: pooled-K cache is NULL");
+  if (reinterpret_cast<uintptr_t>(d_kcache) % 256)
+    return fail(LCSA_ERR_ALIGN, "lcsa_select_ring_rope: pooled-K cache not 256-byte aligned");
+  return lcsa::select_impl("lcsa_select_ring_rope", plan, q, k_ring, ring, new_frames, d_kcache,
+                           d_row_ptr, d_col_idx, d_scores, d_workspace, workspace_bytes, stream,
+                           rope, q_rot, k_rot_ring);
 }
 
 lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,

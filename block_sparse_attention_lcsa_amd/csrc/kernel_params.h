@@ -31,6 +31,22 @@ struct View {
   int64_t sb, ss, sh;    // strides in elements
 };
 
+struct OutView {
+  uint16_t* data;        // bf16 bits
+  int64_t sb, ss, sh;    // strides in elements
+};
+
+// Factored 3D rotary embedding: channel pair j < pt turns by table_t of the
+// token's KV-window frame, pt <= j < pt + ph by table_h of its token row, the
+// rest by table_w of its column; tables hold (cos, sin) float pairs.
+struct RopeParams {
+  const float* table_t;  // [kv_frames][pt][2]
+  const float* table_h;  // [grid_h][ph][2]
+  const float* table_w;  // [grid_w][64 - pt - ph][2]
+  int32_t pt, ph;
+  OutView q_rot, k_rot;  // rotated Q and K (bf16), written by the pool kernel
+};
+
 // Pooled K lives per storage frame, channel pairs innermost:
 // kcache[slot][B*H][64][NBF][2] holds channel 2c + e of position p at [c][p][e].
 struct PoolParams {
@@ -39,6 +55,7 @@ struct PoolParams {
   double* qbar;          // [B][H][NQB][128]
   double* kcache;        // [slots][B*H][64][NBF][2]
   int32_t k_first;       // first KV-window frame whose K blocks are pooled
+  RopeParams rope;       // used by the rotary variant of the pool kernel only
 };
 
 struct SelectParams {

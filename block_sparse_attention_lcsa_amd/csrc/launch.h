@@ -10,7 +10,8 @@
 
 namespace lcsa {
 
-hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStream_t stream);
+hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, bool rope,
+                       hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipStream_t stream);
 hipError_t launch_attend(const AttendParams& p, int block_tokens, hipStream_t stream);
 

@@ -50,11 +50,32 @@ __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, 
   return ((int64_t)t * g.grid_h + y) * g.grid_w + x;
 }
 
+// bf16 bits of a double rounded to the nearest bf16 value, ties to even, in
+// one step (bf16 keeps 7 of the 52 fraction bits of a double).
+__device__ inline uint32_t bf16_rne_bits(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  u = (u + 0xFFFFFFFFFFFull + ((u >> 45) & 1ull)) & ~((1ull << 45) - 1ull);
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;   // exact
+}
+
+// One channel pair (x0, x1) turned by the angle with cosine cs.x and sine
+// cs.y, rounded to bf16: both products are exact in double (8 by 24
+// significant bits), so each component is rounded once, to double, then to
+// bf16.  Returns the two bf16 bit patterns packed (x0' low).
+__device__ inline uint32_t rope_pair(uint32_t w, float2 cs) {
+  const double x0 = bf16_lo(w), x1 = bf16_hi(w);
+  const double r0 = fma(x0, (double)cs.x, -(x1 * (double)cs.y));
+  const double r1 = fma(x0, (double)cs.y, x1 * (double)cs.x);
+  return bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
+}
+
 // grid (NQB + pooled key blocks, heads, batch): x < NQB pools query block x,
 // otherwise key block x - NQB of the KV-window frames k_first onwards, read
 // from (and stored for) their storage frame kv_slot[t].  Thread (c, tg) sums
-// channels 8c..8c+7 of tokens tg, tg+16, ...
-template <int BT>
+// channels 8c..8c+7 of tokens tg, tg+16, ...  With ROPE each 16-byte slice
+// (channel pairs 4c..4c+3) is first turned by the rotary tables, written to
+// the rotated Q / K output, and the rotated bf16 values are what is pooled.
+template <int BT, bool ROPE>
 __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
   __shared__ double red[16 * 128];
   const GridGeom& g = p.g;
@@ -70,10 +91,67 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  // Rotary tables of this thread's four channel pairs: each pair reads the
+  // row of its axis (0 frame, 1 token row, 2 token column) at stride rs.
+  const float2* rtab[4];
+  int raxis[4], rs[4];
+  uint16_t* rot = nullptr;
+  int64_t rot_ss = 0;
+  if constexpr (ROPE) {
+    const RopeParams& rp = p.rope;
+    const int tw = is_q ? g.kv_frames - g.q_frames + t : t;   // KV-window frame
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pr = 4 * c + u;
+      if (pr < rp.pt) {
+        raxis[u] = 0;
+        rs[u] = 0;
+        rtab[u] = reinterpret_cast<const float2*>(rp.table_t) + (int64_t)tw * rp.pt + pr;
+      } else if (pr < rp.pt + rp.ph) {
+        raxis[u] = 1;
+        rs[u] = rp.ph;
+        rtab[u] = reinterpret_cast<const float2*>(rp.table_h) + (pr - rp.pt);
+      } else {
+        raxis[u] = 2;
+        rs[u] = 64 - rp.pt - rp.ph;
+        rtab[u] = reinterpret_cast<const float2*>(rp.table_w) + (pr - rp.pt - rp.ph);
+      }
+    }
+    const OutView& ov = is_q ? rp.q_rot : rp.k_rot;
+    rot = ov.data + (int64_t)b * ov.sb + (int64_t)h * ov.sh + c * 8;
+    rot_ss = ov.ss;
+  }
+  // All loads of the thread first: with the rotary outputs allowed to be the
+  // inputs themselves, the compiler could not move a load above an earlier
+  // token's store.
+  uint4 wv[BT / 16];
+#pragma unroll
+  for (int i = 0; i < BT / 16; ++i)
+    wv[i] = *reinterpret_cast<const uint4*>(base + block_token(g, tf, by, bx, tg + 16 * i) * x.ss + c * 8);
+  // (cos, sin) of every pair of every token, also loaded up front
+  float2 cs[ROPE ? BT / 16 : 1][4];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int i = 0; i < BT / 16; ++i) {
+      const int j = tg + 16 * i;
+      const int y = by * g.block_h + (j >> g.log2_bw), xx = bx * g.block_w + (j & (g.block_w - 1));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pos_a = raxis[u] == 0 ? 0 : raxis[u] == 1 ? y : xx;
+        cs[i][u] = rtab[u][pos_a * rs[u]];
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < BT / 16; ++i) {
     const int j = tg + 16 * i;
-    const uint4 w = *reinterpret_cast<const uint4*>(base + block_token(g, tf, by, bx, j) * x.ss + c * 8);
+    uint4 w = wv[i];
+    if constexpr (ROPE) {
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) wp[u] = rope_pair(wp[u], cs[i][u]);
+      *reinterpret_cast<uint4*>(rot + block_token(g, tf, by, bx, j) * rot_ss) = w;
+    }
     acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
     acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
     acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
@@ -352,12 +430,20 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
 
 }  // namespace
 
-hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, hipStream_t stream) {
+hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, bool rope,
+                       hipStream_t stream) {
   const dim3 grid(p.g.nqb + (p.g.kv_frames - p.k_first) * p.g.nbf, p.g.heads, batch);
-  if (block_tokens == 128)
-    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, stream, p);
+  if (block_tokens == 128) {
+    if (rope)
+      hipLaunchKernelGGL((pool_kernel<128, true>), grid, dim3(kPoolThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pool_kernel<128, false>), grid, dim3(kPoolThreads), 0, stream, p);
+  } else {
+    if (rope)
+      hipLaunchKernelGGL((pool_kernel<64, true>), grid, dim3(kPoolThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pool_kernel<64, false>), grid, dim3(kPoolThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

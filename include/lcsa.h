@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LCSA_ABI_VERSION 3
+#define LCSA_ABI_VERSION 4
 
 typedef int32_t lcsa_status;
 #define LCSA_OK 0
@@ -238,13 +238,74 @@ typedef struct lcsa_kv_ring {
  *                  call with the same batch, heads and grid).
  *  d_kcache        device double[slots * kcache_slot_bytes / 8], caller
  *                  owned and kept between calls, 256-byte aligned; layout
- *                  [slot][batch * heads][128][blocks_per_frame].
+ *                  [slot][batch * heads][64][blocks_per_frame][2]: channel
+ *                  2c + e of the pooled key at block position p sits at
+ *                  [c][p][e].
  *  other arguments as lcsa_select (the workspace holds the pooled Q).
  * Errors: as lcsa_select, plus INVALID (ring or new_frames out of range). */
 lcsa_status lcsa_select_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,
                              const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
                              int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
                              void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Factored 3D rotary position embedding of Q and K, fused into selection.
+ * The DiT turns its queries and keys with a factored 3D RoPE (NxDI FlashVSR
+ * contrib page, "Model Information"), and that pass is part of the attention
+ * glue around the sparse kernel (FlashVSR Hopper PR page, "What Was Actually
+ * Slow"; "How I Fixed It" lists a coalesced RoPE kernel).  Here the pooling
+ * pass of selection, which reads Q and K anyway, turns them, writes the
+ * turned tensors and pools the turned values, so the separate read of Q and
+ * K by a rotary pass goes away.
+ * Channel pair j (channels 2j, 2j + 1, a complex number) turns by:
+ *   j < pairs_t                      the row of table_t for the token's
+ *                                    KV-window frame (a query of query frame
+ *                                    tq is window frame kv_frames - q_frames
+ *                                    + tq),
+ *   pairs_t <= j < pairs_t + pairs_h the row of table_h for its token row,
+ *   the rest                         the row of table_w for its token column.
+ * Tables are float (cos, sin) pairs, row-major [position][pair][2]; the
+ * caller chooses frequencies and the split (pairs_t + pairs_h + pairs_w =
+ * head_dim / 2).  Each turned value x0 cos - x1 sin, x0 sin + x1 cos is
+ * rounded once to bf16 (nearest, ties to even) from its exact value; pooling,
+ * scores and the caller's later lcsa_attend on the outputs see exactly those
+ * bf16 values. */
+typedef struct lcsa_rope {
+  int32_t pairs_t, pairs_h, pairs_w;
+  int32_t reserved;              /* 0 */
+  const float* table_t;          /* device float[kv_frames][pairs_t][2] */
+  const float* table_h;          /* device float[grid_h][pairs_h][2] */
+  const float* table_w;          /* device float[grid_w][pairs_w][2] */
+} lcsa_rope;
+
+/* lcsa_select on the turned Q and K, which it also writes out.
+ *  q, k            unturned inputs, read only.
+ *  rope            the tables (8-byte aligned device pointers).
+ *  q_rot, k_rot    bf16 outputs of the shapes of q and k (own strides,
+ *                  16-byte aligned); may be q and k themselves (each element
+ *                  is read and then written by the same thread).
+ *  other arguments and the CSR result as lcsa_select; pass q_rot and k_rot
+ *  to lcsa_attend.
+ * Errors: as lcsa_select, plus NULL (rope or a table with pairs), INVALID
+ * (pair counts), ALIGN (tables or outputs). */
+lcsa_status lcsa_select_rope(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                             const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                             const lcsa_tensor* k_rot, int32_t* d_row_ptr, int32_t* d_col_idx,
+                             double* d_scores, void* d_workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* lcsa_select_ring with the rotary embedding: the new_frames newest window
+ * frames of k_ring are turned, written to the same ring slots of k_rot_ring
+ * (a ring of the same slots and strides rules) and pooled into d_kcache; the
+ * cache entries of older frames must hold pooled turned keys (an earlier
+ * call of this function).  Q is turned into q_rot.  table_t rows are
+ * KV-window frames of this call.
+ * Errors: as lcsa_select_ring and lcsa_select_rope. */
+lcsa_status lcsa_select_ring_rope(lcsa_plan_t plan, const lcsa_tensor* q,
+                                  const lcsa_tensor* k_ring, const lcsa_kv_ring* ring,
+                                  int32_t new_frames, double* d_kcache, const lcsa_rope* rope,
+                                  const lcsa_tensor* q_rot, const lcsa_tensor* k_rot_ring,
+                                  int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                                  void* d_workspace, size_t workspace_bytes, void* stream);
 
 /* Block-sparse attention with K and V read from a frame ring; otherwise as
  * lcsa_attend (same result as on the contiguous window).

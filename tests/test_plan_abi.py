@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lcsa.abi_version() == 3
+    assert lcsa.abi_version() == 4
     lib = ctypes.CDLL(lcsa.lib_path())
     lib.lcsa_status_string.restype = ctypes.c_char_p
     texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
@@ -203,6 +203,45 @@ def test_ring_entry_point_validation_statuses():
     with pytest.raises(lcsa.LcsaError) as ei:
         lcsa.Plan.from_desc(too_many)
     assert ei.value.name == "LCSA_ERR_SHAPE"
+
+
+def test_rope_entry_point_validation_statuses():
+    """Rotary-embedding arguments are checked on the host before any HIP call."""
+    p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])
+    good = _fake_view()
+    lib = lcsa._lib
+    ws, wsb = 0x40000, p.info["select_workspace_bytes"]
+
+    def rope(pt=22, ph=21, pw=21, tt=0x50000, th=0x60000, tw=0x70000, reserved=0):
+        return lcsa.LcsaRope(pairs_t=pt, pairs_h=ph, pairs_w=pw, reserved=reserved,
+                             table_t=tt, table_h=th, table_w=tw)
+
+    def sel(r, q_rot=good, k_rot=good):
+        rr = ctypes.byref(r) if r is not None else None
+        qr = ctypes.byref(q_rot) if q_rot is not None else None
+        kr = ctypes.byref(k_rot) if k_rot is not None else None
+        return lib.lcsa_select_rope(p.handle, ctypes.byref(good), ctypes.byref(good), rr, qr, kr,
+                                    0x20000, 0x30000, None, ws, wsb, None)
+
+    def sel_ring(r, ring, new=1):
+        rr = ctypes.byref(r) if r is not None else None
+        return lib.lcsa_select_ring_rope(p.handle, ctypes.byref(good), ctypes.byref(good),
+                                         ctypes.byref(ring), new, 0x80000, rr, ctypes.byref(good),
+                                         ctypes.byref(good), 0x20000, 0x30000, None, ws, wsb, None)
+    assert sel(None) == 1                                             # NULL rope
+    assert sel(rope(pt=23)) == 2 and sel(rope(pt=-1, ph=44)) == 2     # pairs must sum to 64
+    assert sel(rope(reserved=1)) == 2
+    assert sel(rope(th=0)) == 1                                       # table with pairs NULL
+    assert sel(rope(pt=0, ph=43, tt=0)) != 1                          # no pairs: table may be NULL
+    assert sel(rope(tw=0x70004)) == 4                                 # ALIGN table
+    assert sel(rope(), q_rot=None) == 1                               # NULL output
+    assert sel(rope(), k_rot=_fake_view(addr=0x10008)) == 4           # ALIGN output
+    assert sel_ring(None, lcsa.kv_ring(4, [3, 0, 1])) == 1
+    assert sel_ring(rope(), lcsa.kv_ring(4, [3, 4, 1])) == 2          # slot out of range
+    assert sel_ring(rope(), lcsa.kv_ring(4, [3, 0, 1]), new=9) == 2
+    if not torch.cuda.is_available():
+        assert sel(rope()) == 6                                       # DEVICE on CPU hosts
+        assert sel_ring(rope(), lcsa.kv_ring(4, [3, 0, 1])) == 6
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device status on CPU hosts")
