@@ -33,6 +33,13 @@ if not os.path.exists(lib_path()):
         "liblcsa.so is not built; run `python block_sparse_attention_lcsa_amd/build_lib.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 
+# torch first: its HIP runtime must be the one in the process before
+# liblcsa.so is loaded.  liblcsa.so asks for libamdhip64.so.7, which the loader
+# then resolves to torch's copy (same soname); loaded the other way round,
+# torch would bring a second HIP runtime, and device pointers and streams from
+# torch would not belong to the runtime liblcsa.so calls.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(lib_path())
 
 # Every symbol include/lcsa.h declares.
