@@ -281,8 +281,10 @@ typedef struct lcsa_rope {
  *  q, k            unturned inputs, read only.
  *  rope            the tables (8-byte aligned device pointers).
  *  q_rot, k_rot    bf16 outputs of the shapes of q and k (own strides,
- *                  16-byte aligned); may be q and k themselves (each element
- *                  is read and then written by the same thread).
+ *                  16-byte aligned); q_rot may be q itself and k_rot k
+ *                  itself (each element is read and then written by the same
+ *                  thread); otherwise they must not overlap each other or
+ *                  the inputs.
  *  other arguments and the CSR result as lcsa_select; pass q_rot and k_rot
  *  to lcsa_attend.
  * Errors: as lcsa_select, plus NULL (rope or a table with pairs), INVALID
