@@ -295,6 +295,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   const float sl2 = p.scale_log2;
 
   int it = next_valid(start);
+  const int first = it;
   if (it < end) {   // K of the first block
     const char* src = kbase + block_offset(col_idx[it], row_stride_k);
 #pragma unroll
@@ -394,7 +395,9 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
       for (int kt = 1; kt < T::kKeyTiles; ++kt) sum += rs[kt];
       return sum;
     };
-    float rsum = make_p(-m_run);
+    // On a row's first block the reference is -inf and P against it would
+    // only be thrown away: go straight to the max.
+    float rsum = it == first ? __builtin_huge_valf() : make_p(-m_run);
     if (__builtin_amdgcn_ballot_w64(!(rsum <= kSumBound)) != 0) {
       // Independent max chains per key tile keep the reduction short.
       float mt[T::kKeyTiles];
@@ -505,8 +508,8 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
 // 16 y + 15; thread t handles query 16 y + t / 16 and channels 8 (t % 16) ..
 // +7, so 16 lanes read one query's 512-byte partial row.  Pieces hold O and
 // the row sum against their own reference m (log2 units); the merge rescales
-// them to a running maximum, four pieces at a time.  A row whose pieces hold no valid block gives O = 0,
-// LSE = -inf.
+// them to a running maximum, four pieces at a time.  A row whose pieces hold
+// no valid block gives O = 0, LSE = -inf.
 constexpr int kMergeThreads = 256;
 template <int BT>
 __global__ void __launch_bounds__(kMergeThreads) attend_merge_kernel(AttendParams p) {
