@@ -164,3 +164,43 @@ def test_select_ring_rope_stream_matches_contiguous():
                                k_ref[:, t * ft:(t + 1) * ft].view(torch.int16)), f"chunk {c} frame {t}"
         say(f"  chunk {c}: window {w0}..{w0 + kvf - 1}, turned and pooled {new} new frames: "
             f"bitwise equal to the contiguous rotary select")
+
+
+def _random_tables(rng, g, pairs):
+    def tab(n, m):
+        ang = rng.uniform(-np.pi, np.pi, size=(n, m))
+        return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    return oracle.RopeTables(t=tab(g.kv_frames, pairs[0]), h=tab(g.grid_h, pairs[1]),
+                             w=tab(g.grid_w, pairs[2]))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_select_rope_random_configs(case):
+    """Random small configurations (as in test_gpu_random_configs) with a
+    random split of the 64 pairs over the three axes and random angles."""
+    from test_gpu_random_configs import random_desc
+    rng = np.random.default_rng(2000 + case)
+    desc = random_desc(rng)
+    cuts = np.sort(rng.integers(0, 65, size=2))
+    pairs = (int(cuts[0]), int(cuts[1] - cuts[0]), int(64 - cuts[1]))
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    tab = _random_tables(rng, g, pairs)
+    dtab = lcsa.rope(*(torch.from_numpy(getattr(tab, a)).cuda() for a in ("t", "h", "w")))
+    say(f"  case {case}: block {desc['block_h']}x{desc['block_w']}, grid {g.nbh}x{g.nbw}, "
+        f"q {g.q_frames} kv {g.kv_frames}, pairs {pairs}")
+    inp = li.generate(desc, seed=100 + case)
+    q, k, v = (to_device_bf16(x) for x in (inp.q, inp.k, inp.v))
+    q_rot, k_rot, rp, ci = lcsa.select_rope(plan, q, k, dtab)
+    o = lcsa.attend(plan, q_rot, k_rot, v, rp, ci)
+    torch.cuda.synchronize()
+    qr = oracle.rope_q(g, li.bf16_bits_to_f64(inp.q), tab)
+    kr = oracle.rope_k(g, li.bf16_bits_to_f64(inp.k), tab)
+    assert np.array_equal(_bits(q_rot), _f64_to_bits(qr))
+    assert np.array_equal(_bits(k_rot), _f64_to_bits(kr))
+    rp_ref, ci_ref, s_ref = oracle.select(g, qr, kr)
+    rp_g, ci_g = rp.cpu().numpy(), ci.cpu().numpy()
+    check_mask(g, rp_ref, ci_ref, s_ref, rp_g, ci_g)
+    o_ref, _ = oracle.attend(g, qr, kr, li.bf16_bits_to_f64(inp.v), rp_g.astype(np.int64),
+                             ci_g.astype(np.int64))
+    compare_output(bf16_to_np(o), o_ref, f"rope random case {case}")
