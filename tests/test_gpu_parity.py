@@ -323,3 +323,39 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_longest_kv_window(ring):
+    """The largest KV window the library takes: 64 latent frames (62 cached +
+    2 query frames), every frame eligible, on a small grid; through the frame
+    ring the 64 frames sit in scrambled slots."""
+    desc = dict(li.CONFIGS["tiny"], heads=1, q_frames=2, cached_frames=62, kv_ratio=0.0, topk=24)
+    plan = lcsa.Plan.from_desc(desc)
+    assert plan.info["kv_frames"] == 64
+    inp = li.generate(desc, seed=4)
+    q, k, v = (to_device_bf16(x) for x in (inp.q, inp.k, inp.v))
+    if ring:
+        ft = desc["grid_h"] * desc["grid_w"]
+        slots = 64
+        frame_slot = np.random.default_rng(3).permutation(slots).tolist()
+        rg = lcsa.kv_ring(slots, frame_slot)
+        k_ring, v_ring = torch.empty_like(k), torch.empty_like(v)
+        for t in range(64):
+            s = frame_slot[t]
+            k_ring[:, s * ft:(s + 1) * ft] = k[:, t * ft:(t + 1) * ft]
+            v_ring[:, s * ft:(s + 1) * ft] = v[:, t * ft:(t + 1) * ft]
+        kcache = torch.empty(lcsa.kcache_bytes(plan, slots) // 8, dtype=torch.float64, device="cuda")
+        rp, ci = lcsa.select_ring(plan, q, k_ring, rg, 64, kcache)
+        o = lcsa.attend_ring(plan, q, k_ring, v_ring, rg, rp, ci)
+    else:
+        rp, ci = lcsa.select(plan, q, k)
+        o = lcsa.attend(plan, q, k, v, rp, ci)
+    torch.cuda.synchronize()
+    g = oracle.geometry(desc)
+    qf, kf, vf = (li.bf16_bits_to_f64(x) for x in (inp.q, inp.k, inp.v))
+    rp_ref, ci_ref, s_ref = oracle.select(g, qf, kf)
+    check_mask(g, rp_ref, ci_ref, s_ref, rp.cpu().numpy(), ci.cpu().numpy())
+    o_ref, _ = oracle.attend(g, qf, kf, vf, rp.cpu().numpy().astype(np.int64),
+                             ci.cpu().numpy().astype(np.int64))
+    compare_output(bf16_to_np(o), o_ref, f"64-frame KV window{' (ring)' if ring else ''}")
