@@ -142,7 +142,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the LCSA path runs per (batch, head) with no "
-              "cross-GPU exchange, and this build has no multi-GPU path. Use --gpus 1.",
+              "cross-GPU exchange, and the library has no multi-GPU code. Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
