@@ -288,8 +288,10 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
             acc[0][r] = fma(q1, cur[u].y, fma(q0, cur[u].x, acc[0][r]));
           }
         }
+        if (dp0 + kU < 64) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
+          for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
+        }
       }
     } else {
 #pragma unroll 2
