@@ -22,6 +22,7 @@ select + attend captured once in a HIP graph.
                   [--cold-steps N] [--graph-steps N]
   python bench.py --workload stream_768x1280 --ring   # streaming steady state
   python bench.py --rope                               # rotary embedding fused into select
+  python bench.py --workload stream_768x1280 --reuse [--ring]   # steady threshold reuse
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -138,6 +139,10 @@ def main():
     ap.add_argument("--ring", action="store_true",
                     help="K/V in a frame ring with the pooled-K cache: each step pools only "
                          "the chunk's q_frames new frames (streaming steady state)")
+    ap.add_argument("--reuse", action="store_true",
+                    help="steady threshold reuse (lcsa_select_reuse): each step selects by the "
+                         "previous chunk's per-row thresholds (from lcsa_select_steady) instead "
+                         "of top-k; streaming workloads only")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -167,6 +172,31 @@ def main():
     info = plan.info
     flops = float(info["useful_flops"])
     ws = torch.empty(max(int(info["select_workspace_bytes"]), 256), dtype=torch.uint8, device=dev)
+    inputs_sha = inp.sha256
+    if args.reuse:
+        # Two consecutive chunks of one synthetic video: the previous chunk
+        # (window frames 0 .. kv_frames-1) gives the thresholds, the current
+        # one (shifted by q_frames) is timed.
+        if desc["cached_frames"] <= 0 or args.rope:
+            print("bench.py: --reuse needs a streaming workload (cached frames) and no --rope",
+                  file=sys.stderr)
+            sys.exit(2)
+        kvf, qf = info["kv_frames"], desc["q_frames"]
+        ft = desc["grid_h"] * desc["grid_w"]
+        video = li.generate(dict(desc, q_frames=kvf + qf, cached_frames=0, kv_ratio=0.0),
+                            seed=args.seed)
+        vk, vv = up(video.k), up(video.v)
+
+        def chunk(c):
+            w0 = c * qf
+            qs = up(video.q[:, (w0 + kvf - qf) * ft:(w0 + kvf) * ft])
+            return (qs, vk[:, w0 * ft:(w0 + kvf) * ft].contiguous(),
+                    vv[:, w0 * ft:(w0 + kvf) * ft].contiguous())
+        q_prev, k_prev, _ = chunk(0)
+        _, _, tau = lcsa.select_steady(plan, q_prev, k_prev, workspace=ws)
+        q, k, v = chunk(1)
+        del vk, vv, q_prev, k_prev, video
+        inputs_sha = None
     att_ws = torch.empty(int(info["attend_workspace_bytes"]), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
@@ -195,16 +225,23 @@ def main():
         lcsa.select_ring(plan, q, k_ring, ring, kvf, kcache, workspace=ws)
         new_frames = min(desc["q_frames"], kvf)
 
+    def do_select(p):
+        if args.reuse and args.ring:
+            return lcsa.select_reuse(p, q, k_ring, tau, ring=ring, new_frames=new_frames,
+                                     kcache=kcache, workspace=ws)
+        if args.reuse:
+            return lcsa.select_reuse(p, q, k, tau, workspace=ws)
+        if args.ring:
+            return lcsa.select_ring(p, q, k_ring, ring, new_frames, kcache, workspace=ws)
+        if args.rope:
+            return lcsa.select_rope(p, q, k, rtab, q_rot=q_rot, k_rot=k_rot, workspace=ws)[2:]
+        return lcsa.select(p, q, k, workspace=ws)
+
     def step(ev=None):
         p = lcsa.Plan.from_desc(desc)                      # host plan (per shape)
         if ev:
             ev[0].record(stream)
-        if args.ring:
-            rp, ci = lcsa.select_ring(p, q, k_ring, ring, new_frames, kcache, workspace=ws)
-        elif args.rope:
-            _, _, rp, ci = lcsa.select_rope(p, q, k, rtab, q_rot=q_rot, k_rot=k_rot, workspace=ws)
-        else:
-            rp, ci = lcsa.select(p, q, k, workspace=ws)
+        rp, ci = do_select(p)
         if ev:
             ev[1].record(stream)
         if args.ring:
@@ -263,15 +300,12 @@ def main():
         gplan = lcsa.Plan.from_desc(desc)
 
         def graph_body():
+            rp, ci = do_select(gplan)
             if args.ring:
-                rp, ci = lcsa.select_ring(gplan, q, k_ring, ring, new_frames, kcache, workspace=ws)
                 lcsa.attend_ring(gplan, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
             elif args.rope:
-                _, _, rp, ci = lcsa.select_rope(gplan, q, k, rtab, q_rot=q_rot, k_rot=k_rot,
-                                                workspace=ws)
                 lcsa.attend(gplan, q_rot, k_rot, v, rp, ci, out=out, workspace=att_ws)
             else:
-                rp, ci = lcsa.select(gplan, q, k, workspace=ws)
                 lcsa.attend(gplan, q, k, v, rp, ci, out=out, workspace=att_ws)
             return rp, ci
 
@@ -300,18 +334,19 @@ def main():
     # Rotary embedding: the fused select against plain select on the same
     # inputs plus a device copy of Q and K, the least a separate rotary pass
     # (read Q and K, write the turned tensors) would cost.
+    def tmed(fn, n=20):
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts]))
+
     rope_cmp = None
     if args.rope:
-        def tmed(fn, n=20):
-            ts = []
-            for _ in range(n):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                ts.append((e0, e1))
-            torch.cuda.synchronize()
-            return float(np.median([a.elapsed_time(b) for a, b in ts]))
         rope_plan = lcsa.Plan.from_desc(desc)
         for _ in range(3):
             lcsa.select(rope_plan, q, k, workspace=ws)
@@ -327,6 +362,51 @@ def main():
                     "qk_copy_ms_median": copy_ms,
                     "separate_pass_lower_bound_ms": plain_ms + copy_ms}
 
+    # Threshold reuse against top-k on the same (current) chunk: times of
+    # both selections and of attention on both masks, and how far the reused
+    # mask and its output are from top-k's.
+    reuse_cmp = None
+    n_idx = int(info["nnz"])
+    if args.reuse:
+        rplan = lcsa.Plan.from_desc(desc)
+        rows, nkb, pad = int(info["rows"]), int(info["nkb"]), int(info["max_window"])
+        rp_r, ci_r = do_select(rplan)
+        rp_t, ci_t = lcsa.select(rplan, q, k, workspace=ws)
+        o_t, o_r = torch.empty_like(q), torch.empty_like(q)
+        lcsa.attend(rplan, q, k, v, rp_t, ci_t, out=o_t, workspace=att_ws)
+        lcsa.attend(rplan, q, k, v, rp_r, ci_r, out=o_r, workspace=att_ws)
+        torch.cuda.synchronize()
+        n_idx = ci_r.numel()
+        cr = ci_r.view(rows, pad).long()
+        kept = (cr >= 0).sum(dim=1)
+        m_r = torch.zeros(rows, nkb + 1, dtype=torch.bool, device=dev)
+        m_r.scatter_(1, torch.where(cr >= 0, cr, nkb), True)
+        rl = (rp_t[1:] - rp_t[:-1]).long()
+        m_t = torch.zeros(rows, nkb, dtype=torch.bool, device=dev)
+        m_t[torch.repeat_interleave(torch.arange(rows, device=dev), rl), ci_t.long()] = True
+        both = int((m_t & m_r[:, :nkb]).sum())
+        kept_pairs = int(kept.sum())
+        flops = float(info["useful_flops"]) * kept_pairs / max(int(info["nnz"]), 1)
+        of_t, of_r = o_t.float(), o_r.float()
+        reuse_cmp = {
+            "thresholds": "previous chunk's per-row k-th window score (lcsa_select_steady)",
+            "kept_pairs": kept_pairs, "top_k_pairs": int(info["nnz"]),
+            "kept_per_row_mean": float(kept.float().mean()),
+            "kept_per_row_min": int(kept.min()), "kept_per_row_max": int(kept.max()),
+            "rows_keeping_none": int((kept == 0).sum()),
+            "recall_of_top_k": both / max(int(info["nnz"]), 1),
+            "precision_vs_top_k": both / max(kept_pairs, 1),
+            "output_rel_l2_vs_top_k": float((of_r - of_t).norm() / of_t.norm()),
+            "output_max_abs_vs_top_k": float((of_r - of_t).abs().max()),
+            "select_reuse_ms_median": tmed(lambda: do_select(rplan)),
+            "select_top_k_ms_median": tmed(lambda: lcsa.select(rplan, q, k, workspace=ws)),
+            "attend_reused_mask_ms_median": tmed(
+                lambda: lcsa.attend(rplan, q, k, v, rp_r, ci_r, out=o_r, workspace=att_ws)),
+            "attend_top_k_mask_ms_median": tmed(
+                lambda: lcsa.attend(rplan, q, k, v, rp_t, ci_t, out=o_t, workspace=att_ws)),
+        }
+        del m_r, m_t, o_t, o_r
+
     att_avg = float(np.mean(att_ms))
     sel_avg = float(np.mean(sel_ms))
     step_ms = max(wall_ms, gpu_ms)
@@ -336,7 +416,7 @@ def main():
     pooled_kv_tokens = info["kv_tokens"] * new_frames // info["kv_frames"]
     qk_bytes = 2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + pooled_kv_tokens)
     # with the rotary embedding the turned Q and K are written as well
-    sel_bytes = qk_bytes * (2 if args.rope else 1) + 4 * (info["rows"] + 1 + info["nnz"])
+    sel_bytes = qk_bytes * (2 if args.rope else 1) + 4 * (info["rows"] + 1 + n_idx)
     sel_gbs = sel_bytes / (sel_avg * 1e-3) / 1e9
 
     res = {
@@ -357,8 +437,11 @@ def main():
             "batch": desc["batch"], "heads": desc["heads"], "head_dim": desc["head_dim"],
             "q_tokens": info["q_tokens"], "kv_tokens": info["kv_tokens"],
             "block": [info["block_h"], info["block_w"]], "local_range": desc["local_range"],
-            "k": info["k"], "selected_pairs": info["nnz"], "useful_tflop": flops / 1e12,
-            "seed": args.seed, "inputs_sha256": inp.sha256,
+            "k": info["k"],
+            "selected_pairs": reuse_cmp["kept_pairs"] if args.reuse else info["nnz"],
+            "useful_tflop": flops / 1e12,
+            "seed": args.seed, "inputs_sha256": inputs_sha,
+            "selection": "threshold reuse" if args.reuse else "top-k",
             "kv_storage": "frame ring + pooled-K cache" if args.ring else "contiguous window",
             "rope": "factored 3D, fused into select (22/21/21 pairs)" if args.rope else None,
             "pooled_kv_frames": new_frames,
@@ -374,6 +457,7 @@ def main():
         "cold_cache": cold,
         "graph": graph,
         "rope_fusion": rope_cmp,
+        "threshold_reuse": reuse_cmp,
         "attend_tflops": achieved,
         "attend_frac_of_bf16_peak": achieved / PEAK_BF16_TFLOPS,
         "roofline": {
@@ -394,7 +478,7 @@ def main():
         },
         "device": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.reuse:
         res["cpu_baseline"] = cpu_baseline(name, desc, inp, flops, tabs if args.rope else None)
     print(json.dumps(res), flush=True)
 

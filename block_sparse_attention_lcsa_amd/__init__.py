@@ -19,7 +19,7 @@ import ctypes
 import os
 
 __all__ = ["Plan", "LcsaError", "select", "attend", "select_ring", "attend_ring", "select_rope",
-           "select_ring_rope", "rope", "lib_path", "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
+           "select_ring_rope", "rope", "select_steady", "select_reuse", "lib_path", "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -46,7 +46,8 @@ _lib = ctypes.CDLL(lib_path())
 EXPORTS = [
     "lcsa_plan_create", "lcsa_plan_destroy", "lcsa_plan_get_info", "lcsa_plan_row_ptr",
     "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_select_rope",
-    "lcsa_select_ring_rope", "lcsa_select_ring", "lcsa_attend_ring",
+    "lcsa_select_ring_rope", "lcsa_select_ring", "lcsa_attend_ring", "lcsa_select_steady",
+    "lcsa_select_reuse",
     "lcsa_status_string", "lcsa_last_error", "lcsa_abi_version",
 ]
 MAX_KV_FRAMES = 64
@@ -138,6 +139,18 @@ _lib.lcsa_attend_ring.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER
                                   ctypes.c_int64, ctypes.POINTER(LcsaTensor), _P, _P,
                                   ctypes.c_size_t, _P]
 _lib.lcsa_attend_ring.restype = ctypes.c_int32
+_lib.lcsa_select_steady.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                    ctypes.POINTER(LcsaKvRing), ctypes.c_int32, _P,
+                                    ctypes.POINTER(LcsaRope), ctypes.POINTER(LcsaTensor),
+                                    ctypes.POINTER(LcsaTensor), _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]
+_lib.lcsa_select_steady.restype = ctypes.c_int32
+_lib.lcsa_select_reuse.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                   ctypes.POINTER(LcsaKvRing), ctypes.c_int32, _P,
+                                   ctypes.POINTER(LcsaRope), ctypes.POINTER(LcsaTensor),
+                                   ctypes.POINTER(LcsaTensor), _P, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]
+_lib.lcsa_select_reuse.restype = ctypes.c_int32
 _lib.lcsa_status_string.argtypes = [ctypes.c_int32]
 _lib.lcsa_status_string.restype = ctypes.c_char_p
 _lib.lcsa_last_error.argtypes = []
@@ -524,3 +537,88 @@ def select_ring_rope(plan: Plan, q, k_ring, ring: LcsaKvRing, new_frames: int, k
                                     _stream_ptr(q, stream))
     _check(st, "lcsa_select_ring_rope")
     return q_rot, row_ptr, col_idx
+
+
+def _threshold_select(fn, plan: Plan, q, k, tau, ring, new_frames, kcache, tables, q_rot, k_rot,
+                      return_scores, workspace, stream):
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    if ring is not None:
+        _check_ring_tensor(k, plan, ring.slots, "k")
+        if kcache is None or kcache.dtype != torch.float64 or \
+                kcache.numel() * 8 < kcache_bytes(plan, ring.slots):
+            raise ValueError("kcache must be float64 with kcache_bytes(plan, slots) bytes")
+    else:
+        _check_shape(k, plan, "kv_tokens", "k")
+    if tables is not None:
+        tables.check(plan)
+        if q_rot is None or k_rot is None:
+            raise ValueError("with rotary tables pass q_rot and k_rot (they may be q and k)")
+        _check_shape(q_rot, plan, "q_tokens", "q_rot")
+        if ring is not None:
+            _check_ring_tensor(k_rot, plan, ring.slots, "k_rot")
+        else:
+            _check_shape(k_rot, plan, "kv_tokens", "k_rot")
+    inf = plan.info
+    dev = q.device
+    rows = int(inf["rows"])
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if tau is None:
+        n_idx = int(inf["nnz"])
+        kth = torch.empty(rows, dtype=torch.float64, device=dev)
+    else:
+        if tau.dtype != torch.float64 or tau.numel() != rows or not tau.is_contiguous():
+            raise ValueError(f"tau must be contiguous float64 [{rows}]")
+        n_idx = rows * int(inf["max_window"])
+        kth = None
+    col_idx = torch.empty(max(n_idx, 1), dtype=torch.int32, device=dev)[:n_idx]
+    if workspace is None:
+        workspace = torch.empty(max(int(inf["select_workspace_bytes"]), 256), dtype=torch.uint8,
+                                device=dev)
+    scores = None
+    if return_scores:
+        d = plan.desc
+        scores = torch.empty((d["batch"], d["heads"], inf["nqb"], inf["nkb"]),
+                             dtype=torch.float64, device=dev)
+    qv, kv = tensor_view(q), tensor_view(k)
+    rope_p = ctypes.byref(tables.desc) if tables is not None else None
+    qr = ctypes.byref(tensor_view(q_rot)) if tables is not None else None
+    kr = ctypes.byref(tensor_view(k_rot)) if tables is not None else None
+    ring_p = ctypes.byref(ring) if ring is not None else None
+    kc = kcache.data_ptr() if ring is not None else None
+    common = (plan.handle, ctypes.byref(qv), ctypes.byref(kv), ring_p,
+              int(new_frames) if ring is not None else 0, kc, rope_p, qr, kr)
+    tail = (scores.data_ptr() if scores is not None else None, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_ptr(q, stream))
+    ci = col_idx.data_ptr() if n_idx else None
+    if tau is None:
+        st = _lib.lcsa_select_steady(*common, row_ptr.data_ptr(), ci, kth.data_ptr(), *tail)
+    else:
+        st = _lib.lcsa_select_reuse(*common, tau.data_ptr(), row_ptr.data_ptr(), ci, *tail)
+    _check(st, fn)
+    out = (row_ptr, col_idx) if tau is not None else (row_ptr, col_idx, kth)
+    return out + (scores,) if return_scores else out
+
+
+def select_steady(plan: Plan, q, k, ring: LcsaKvRing = None, new_frames: int = 0, kcache=None,
+                  tables: "RopeTables" = None, q_rot=None, k_rot=None,
+                  return_scores: bool = False, workspace=None, stream=None):
+    """Top-k selection that also returns each CSR row's threshold (its
+    keep-th largest window score, float64 [rows]) for select_reuse.  With
+    ring, k is the K ring and kcache the pooled-K cache as in select_ring;
+    with tables, q and k are turned into q_rot and k_rot (which may be q and
+    k) as in select_rope.  Returns (row_ptr, col_idx, kth[, scores])."""
+    return _threshold_select("lcsa_select_steady", plan, q, k, None, ring, new_frames, kcache,
+                             tables, q_rot, k_rot, return_scores, workspace, stream)
+
+
+def select_reuse(plan: Plan, q, k, tau, ring: LcsaKvRing = None, new_frames: int = 0,
+                 kcache=None, tables: "RopeTables" = None, q_rot=None, k_rot=None,
+                 return_scores: bool = False, workspace=None, stream=None):
+    """Selection by per-row thresholds tau (float64 [rows], e.g. the kth of
+    an earlier select_steady): row r keeps its window blocks scored >= tau[r].
+    Returns the padded CSR (row_ptr = r * max_window, col_idx int32
+    [rows * max_window] with -1 after each row's blocks[, scores]); attend
+    accepts it as it is."""
+    return _threshold_select("lcsa_select_reuse", plan, q, k, tau, ring, new_frames, kcache,
+                             tables, q_rot, k_rot, return_scores, workspace, stream)

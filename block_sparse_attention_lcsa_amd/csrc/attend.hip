@@ -205,16 +205,6 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   const int tq = qb / g.nbf, qpos = qb - tq * g.nbf;
   const int qby = qpos / g.nbw, qbx = qpos - qby * g.nbw;
 
-  // Q fragments (MFMA operand B of S^T): query lane&31, channels 16s+8*half..+7.
-  const int qi = wave * 32 + l32;
-  const int64_t qtok = block_token(g, tq, qby, qbx, qi);
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qrow = p.q.data + (int64_t)b * p.q.sb + qtok * p.q.ss + (int64_t)h * p.q.sh;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(load16(qrow + 16 * s + 8 * half));
-  }
-
   // The CSR is read-only here: read it through the constant address space so
   // the (uniform) reads become scalar loads, which do not wait on the vector
   // memory counter that tracks the in-flight tile loads.
@@ -227,6 +217,28 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   int start = row_ptr[row], end = row_ptr[row + 1];
   start = start < 0 ? 0 : (start > nnz ? nnz : start);
   end = end < start ? start : (end > nnz ? nnz : end);
+  // Entries outside [0, nkb) at the row's end (the -1 padding of a
+  // threshold selection) are cut off before the row is split or walked, so
+  // that a split row's pieces share its blocks evenly and a whole row does
+  // not step through them one by one: one scalar load when the row ends in
+  // a valid block, else one wave-wide look per 64 entries from the end.
+  if (end > start) {
+    const int last = col_idx[end - 1];
+    if (last < 0 || last >= g.nkb) {
+      int e = end, cut = start;
+      while (e > start) {
+        const int i = e - 64 + lane;
+        const int kb = i >= start ? p.col_idx[i] : -1;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(kb >= 0 && kb < g.nkb);
+        if (m) {
+          cut = e - 64 + (64 - __clzll(m));
+          break;
+        }
+        e -= 64;
+      }
+      end = cut;
+    }
+  }
   if (piece >= 0) {
     // consecutive parts of the row's CSR range
     const int64_t len = end - start;
@@ -236,6 +248,16 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   }
   start = __builtin_amdgcn_readfirstlane(start);
   end = __builtin_amdgcn_readfirstlane(end);
+
+  // Q fragments (MFMA operand B of S^T): query lane&31, channels 16s+8*half..+7.
+  const int qi = wave * 32 + l32;
+  const int64_t qtok = block_token(g, tq, qby, qbx, qi);
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qrow = p.q.data + (int64_t)b * p.q.sb + qtok * p.q.ss + (int64_t)h * p.q.sh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(load16(qrow + 16 * s + 8 * half));
+  }
 
   // Per-lane byte offsets (inside one key block) of the 8 direct loads of a
   // tile: load i of wave w fills LDS slots [(i*waves + w)*64, +64); slot s

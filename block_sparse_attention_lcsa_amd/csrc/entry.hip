@@ -159,7 +159,8 @@ lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
                         double* d_kcache, int32_t* d_row_ptr, int32_t* d_col_idx,
                         double* d_scores, void* d_workspace, size_t workspace_bytes,
                         void* stream, const lcsa_rope* rope = nullptr,
-                        const lcsa_tensor* q_rot = nullptr, const lcsa_tensor* k_rot = nullptr) {
+                        const lcsa_tensor* q_rot = nullptr, const lcsa_tensor* k_rot = nullptr,
+                        double* d_kth = nullptr, const double* d_tau = nullptr) {
   if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
@@ -167,6 +168,11 @@ lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   if ((st = check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
   if (rope && (st = check_rope(fn, rope, q_rot, k_rot))) return st;
   if (!d_row_ptr || !d_col_idx) return fail(LCSA_ERR_NULL, "%s: CSR buffers are NULL", fn);
+  if (d_tau && in.rows * static_cast<int64_t>(in.max_window) >= INT32_MAX)
+    return fail(LCSA_ERR_SHAPE, "%s: %lld rows of %d entries exceed int32 CSR", fn,
+                (long long)in.rows, in.max_window);
+  if ((reinterpret_cast<uintptr_t>(d_kth) | reinterpret_cast<uintptr_t>(d_tau)) % 8)
+    return fail(LCSA_ERR_ALIGN, "%s: threshold arrays must be 8-byte aligned", fn);
   if (in.max_window > kMaxWindow)
     return fail(LCSA_ERR_SHAPE, "window of %d key blocks exceeds the select limit of %d",
                 in.max_window, kMaxWindow);
@@ -211,6 +217,9 @@ lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   sp.row_ptr = d_row_ptr;
   sp.col_idx = d_col_idx;
   sp.scores = d_scores;
+  sp.kth = d_kth;
+  sp.tau = d_tau;
+  sp.pad = in.max_window;
   e = launch_select(sp, plan->desc.batch, in.max_window, s);
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "select launch: %s", hipGetErrorString(e));
   return LCSA_OK;
@@ -294,6 +303,31 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   return LCSA_OK;
 }
 
+// Shared body of lcsa_select_steady and lcsa_select_reuse: the ring and the
+// rotary tables are each optional.
+lcsa_status threshold_select_impl(const char* fn, lcsa_plan_t plan, const lcsa_tensor* q,
+                                  const lcsa_tensor* k, const lcsa_kv_ring* ring,
+                                  int32_t new_frames, double* d_kcache, const lcsa_rope* rope,
+                                  const lcsa_tensor* q_rot, const lcsa_tensor* k_rot,
+                                  int32_t* d_row_ptr, int32_t* d_col_idx, double* d_kth,
+                                  const double* d_tau, double* d_scores, void* d_workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
+  if (ring) {
+    lcsa_status st;
+    if ((st = check_ring(fn, plan, ring))) return st;
+    if (new_frames < 0 || new_frames > plan->info.kv_frames)
+      return fail(LCSA_ERR_INVALID, "%s: new_frames %d outside [0, %d]", fn, new_frames,
+                  plan->info.kv_frames);
+    if (!d_kcache) return fail(LCSA_ERR_NULL, "%s: pooled-K cache is NULL", fn);
+    if (reinterpret_cast<uintptr_t>(d_kcache) % 256)
+      return fail(LCSA_ERR_ALIGN, "%s: pooled-K cache not 256-byte aligned", fn);
+  }
+  return select_impl(fn, plan, q, k, ring, ring ? new_frames : 0, ring ? d_kcache : nullptr,
+                     d_row_ptr, d_col_idx, d_scores, d_workspace, workspace_bytes, stream, rope,
+                     q_rot, k_rot, d_kth, d_tau);
+}
+
 }  // namespace lcsa
 
 using lcsa::fail;
@@ -358,6 +392,32 @@ lcsa_status lcsa_select_ring_rope(lcsa_plan_t plan, const lcsa_tensor* q,
   return lcsa::select_impl("lcsa_select_ring_rope", plan, q, k_ring, ring, new_frames, d_kcache,
                            d_row_ptr, d_col_idx, d_scores, d_workspace, workspace_bytes, stream,
                            rope, q_rot, k_rot_ring);
+}
+
+lcsa_status lcsa_select_steady(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                               const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
+                               const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                               const lcsa_tensor* k_rot, int32_t* d_row_ptr, int32_t* d_col_idx,
+                               double* d_kth, double* d_scores, void* d_workspace,
+                               size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  if (!d_kth) return fail(LCSA_ERR_NULL, "lcsa_select_steady: kth is NULL");
+  return lcsa::threshold_select_impl("lcsa_select_steady", plan, q, k, ring, new_frames,
+                                     d_kcache, rope, q_rot, k_rot, d_row_ptr, d_col_idx, d_kth,
+                                     nullptr, d_scores, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_select_reuse(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                              const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
+                              const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                              const lcsa_tensor* k_rot, const double* d_tau, int32_t* d_row_ptr,
+                              int32_t* d_col_idx, double* d_scores, void* d_workspace,
+                              size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  if (!d_tau) return fail(LCSA_ERR_NULL, "lcsa_select_reuse: tau is NULL");
+  return lcsa::threshold_select_impl("lcsa_select_reuse", plan, q, k, ring, new_frames, d_kcache,
+                                     rope, q_rot, k_rot, d_row_ptr, d_col_idx, nullptr, d_tau,
+                                     d_scores, d_workspace, workspace_bytes, stream);
 }
 
 lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,

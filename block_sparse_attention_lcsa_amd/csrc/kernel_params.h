@@ -66,6 +66,13 @@ struct SelectParams {
   int32_t* row_ptr;
   int32_t* col_idx;
   double* scores;        // optional [B][H][NQB][NKB]
+  // Top-k selection (tau == nullptr): optional [rows] output, each row's
+  // keep-th largest window score.  Threshold selection (tau set): row r
+  // keeps the window blocks scored >= tau[r], written to col_idx entries
+  // [r * pad, (r + 1) * pad) in ascending order, then -1 to the row's end.
+  double* kth;
+  const double* tau;
+  int32_t pad;
 };
 
 struct AttendParams {

@@ -26,6 +26,15 @@
 // it are kept; keys equal to it are kept in ascending block order until k
 // are kept (ties go to the lower block index).  The bits that all keys of a
 // row share (found from a wave-wide OR and AND) need no count.
+//
+// Steady threshold reuse (FlashVSR Hopper PR page, "Remove the remaining
+// control-plane tax" and "Recommended GH200 Controls": a steady chunk's
+// mask threshold is kept per DiT block and reused): the top-k run can also
+// write each row's keep-th largest window score, and a threshold run keeps,
+// instead of the top-k, every window block scored at or above its row's
+// given threshold.  Threshold rows vary in length, so they are written at a
+// fixed width (the largest window) with -1 after the kept blocks; attention
+// skips -1 entries and trims them from a row's end.
 
 #include <hip/hip_runtime.h>
 
@@ -322,7 +331,7 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   // CSR offset of these rows: rows run (b, h, frame, position); every frame
   // holds the same per-position counts min(k, |window(position)|).
   int lt = 0, all = 0;
-  for (int q = lane; q < g.nbf; q += 64) {
+  for (int q = p.tau ? g.nbf : lane; q < g.nbf; q += 64) {
     const int qy = q / g.nbw, qx = q - qy * g.nbw;
     const int c = min(g.k, window_box(g, qy, qx).n);
     all += c;
@@ -359,6 +368,26 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
 #pragma unroll
       for (int j = 0; j < M; ++j)
         if (valid[j]) srow[kb[j]] = s[j];
+    }
+    if (p.tau) {
+      // Threshold selection: the window blocks at or above the row's
+      // threshold, ascending, then -1 up to the row's fixed width.
+      const double th = p.tau[row];
+      const int64_t off = row * (int64_t)p.pad;
+      if (lane == 0) {
+        p.row_ptr[row + 1] = (int32_t)(off + p.pad);
+        if (row == 0) p.row_ptr[0] = 0;
+      }
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const bool keep_j = valid[j] && s[j] >= th;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(keep_j);
+        if (keep_j) p.col_idx[off + base + __popcll(m & below)] = kb[j];
+        base += __popcll(m);
+      }
+      for (int x = base + lane; x < p.pad; x += 64) p.col_idx[off + x] = -1;
+      continue;
     }
     const int64_t off = (bh * g.q_frames + tq) * (int64_t)all + lt;
     if (lane == 0) {
@@ -417,6 +446,15 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
           need = need < 0 ? 0 : need;
         }
       }
+    }
+
+    if (p.kth) {  // the smallest kept score is the keep-th largest
+      double mn = __builtin_huge_val();
+#pragma unroll
+      for (int j = 0; j < M; ++j) mn = sel[j] ? fmin(mn, s[j]) : mn;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) mn = fmin(mn, __shfl_xor(mn, m));
+      if (lane == 0) p.kth[row] = mn;
     }
 
     // Emit kept blocks in ascending candidate (= key block) order.

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LCSA_ABI_VERSION 4
+#define LCSA_ABI_VERSION 5
 
 typedef int32_t lcsa_status;
 #define LCSA_OK 0
@@ -308,6 +308,53 @@ lcsa_status lcsa_select_ring_rope(lcsa_plan_t plan, const lcsa_tensor* q,
                                   const lcsa_tensor* q_rot, const lcsa_tensor* k_rot_ring,
                                   int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
                                   void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Steady threshold reuse.  The final GH200 configuration of the FlashVSR
+ * Hopper PR page keeps, per DiT block, the mask threshold of a steady chunk
+ * and reuses it for later chunks instead of ranking the scores again
+ * ("Remove the remaining control-plane tax"; quality-gated in "Recommended
+ * GH200 Controls").  The page does not define the threshold; here it is
+ * each CSR row's keep-th largest window score (keep = min(k, |window|)),
+ * which with the same scores and no tie at that score selects exactly the
+ * top-k.  A reused threshold selects by the new chunk's scores: the kept
+ * count varies by row, from none to the whole window, so the result is an
+ * approximation of top-k, not equal to it.
+ *
+ * Both calls take the forms of the selections above: ring == NULL reads k as
+ * the contiguous window (new_frames and d_kcache ignored), otherwise as
+ * lcsa_select_ring; rope == NULL takes q and k as already turned (q_rot and
+ * k_rot ignored), otherwise as lcsa_select_rope / lcsa_select_ring_rope.
+ *
+ * lcsa_select_steady: the top-k selection of those forms (same CSR), plus
+ *  d_kth           device double[rows], 8-byte aligned, written: row r's
+ *                  keep-th largest window score (rows in CSR order).
+ * Errors: as the form used, plus NULL (d_kth), ALIGN (d_kth). */
+lcsa_status lcsa_select_steady(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                               const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
+                               const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                               const lcsa_tensor* k_rot, int32_t* d_row_ptr, int32_t* d_col_idx,
+                               double* d_kth, double* d_scores, void* d_workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* lcsa_select_reuse: selection by threshold instead of top-k.
+ *  d_tau           device double[rows], 8-byte aligned, read: row r keeps
+ *                  every window block whose float64 pooled score is >= d_tau[r]
+ *                  (-inf keeps the whole window; +inf or NaN keeps nothing).
+ *  d_row_ptr       device int32[rows + 1], written: r * max_window.
+ *  d_col_idx       device int32[rows * max_window], written: row r's kept
+ *                  blocks ascending, then -1 to the end of its max_window
+ *                  entries.  Pass it to lcsa_attend / lcsa_attend_ring with
+ *                  nnz = rows * max_window: attention skips -1 entries, and a
+ *                  row that keeps nothing gives O = 0 and LSE = -inf.
+ *  d_scores        as lcsa_select (the scores compared with d_tau).
+ * Errors: as the form used, plus NULL (d_tau), ALIGN (d_tau), SHAPE
+ * (rows * max_window >= 2^31). */
+lcsa_status lcsa_select_reuse(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                              const lcsa_kv_ring* ring, int32_t new_frames, double* d_kcache,
+                              const lcsa_rope* rope, const lcsa_tensor* q_rot,
+                              const lcsa_tensor* k_rot, const double* d_tau, int32_t* d_row_ptr,
+                              int32_t* d_col_idx, double* d_scores, void* d_workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Block-sparse attention with K and V read from a frame ring; otherwise as
  * lcsa_attend (same result as on the contiguous window).

@@ -1,0 +1,222 @@
+"""Steady threshold reuse through the C ABI (lcsa_select_steady /
+lcsa_select_reuse) against the float64 oracle (oracle/threshold_oracle.py).
+
+Steady: the CSR is the top-k selection's, bit for bit; each row's threshold
+is its keep-th largest window score (exactly the smallest kept GPU score,
+and within 1e-12 of the row scale of the oracle's).  Reuse: the padded CSR
+keeps exactly the oracle's blocks, except blocks whose oracle score lies
+within 1e-9 of the score scale of the threshold (the two sides' float64
+scores differ by ~1e-16 relative); thresholds of the same chunk give back
+the top-k.  Attend on the padded CSR equals attend on the same blocks
+compacted, bit for bit, and matches the oracle's attention on it."""
+import numpy as np
+import pytest
+import torch
+
+import lcsa_inputs as li
+import oracle
+from gpu_util import bf16_to_np, compare_output, device_qkv, host_inputs, oracle_select, say
+
+pytestmark = pytest.mark.gpu
+
+import block_sparse_attention_lcsa_amd as lcsa  # noqa: E402  (fails loudly if not built)
+
+SMALL = ["tiny", "tiny_window", "small_edges", "small_16x8"]
+BAND = 1e-9
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say(f"[gpu] start {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+    say(f"[gpu] done  {request.node.nodeid}")
+
+
+def _rows(g):
+    for b in range(g.batch):
+        for h in range(g.heads):
+            for qb in range(g.nqb):
+                yield (b * g.heads + h) * g.nqb + qb, b, h, qb
+
+
+def _check_padded(g, rp, ci, pad):
+    rows = g.batch * g.heads * g.nqb
+    assert np.array_equal(rp, np.arange(rows + 1) * pad)
+    out = []
+    for r, b, h, qb in _rows(g):
+        seg = ci[r * pad:(r + 1) * pad]
+        n = int(np.sum(seg >= 0))
+        assert np.all(seg[n:] == -1), f"row {r}: -1 padding not at the end"
+        blocks = seg[:n]
+        assert np.all(np.diff(blocks) > 0), f"row {r}: not ascending"
+        assert set(blocks.tolist()) <= set(oracle.window(g, qb).tolist()), f"row {r}: off window"
+        out.append(blocks)
+    return out
+
+
+def _compare_with_oracle(g, rows_gpu, s_ref, tau, label):
+    rows_ref = oracle.select_threshold(g, s_ref, tau)
+    scale = float(np.abs(s_ref[np.isfinite(s_ref)]).max())
+    diff_rows = 0
+    for (r, b, h, qb), a, e in zip(_rows(g), rows_gpu, rows_ref):
+        if np.array_equal(a, e):
+            continue
+        diff_rows += 1
+        for kb in set(a.tolist()) ^ set(e.tolist()):
+            assert abs(s_ref[b, h, qb, kb] - tau[r]) <= BAND * scale, \
+                f"{label} row {r} block {kb}: differs and is not at the threshold"
+    kept = np.array([len(a) for a in rows_gpu])
+    say(f"  {label}: kept per row mean {kept.mean():.2f} (min {kept.min()}, max {kept.max()}), "
+        f"rows differing at the threshold {diff_rows}")
+    return kept
+
+
+@pytest.mark.parametrize("name", SMALL + ["stream_768x1280", "first_768x1280"])
+def test_steady_is_top_k_with_thresholds(name):
+    desc, q, k, _ = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp0, ci0 = lcsa.select(plan, q, k)
+    rp, ci, kth, sc = lcsa.select_steady(plan, q, k, return_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp0) and torch.equal(ci, ci0)
+    g, _, _, s_ref = oracle_select(name)
+    rp_h, ci_h, kth_h, sc_h = (x.cpu().numpy() for x in (rp, ci, kth, sc))
+    for r, b, h, qb in _rows(g):
+        kept = ci_h[rp_h[r]:rp_h[r + 1]]
+        assert kth_h[r] == sc_h[b, h, qb, kept].min(), f"row {r}: kth is not the smallest kept"
+    want = oracle.row_thresholds(g, s_ref)
+    scale = float(np.abs(s_ref[np.isfinite(s_ref)]).max())
+    err = float(np.abs(kth_h - want).max())
+    say(f"  {name}: kth max|err| {err:.3e} (scale {scale:.3e})")
+    assert err <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("name", SMALL + ["stream_768x1280"])
+def test_reuse_parity(name):
+    """Thresholds of another chunk (seed 1) applied to this chunk's scores."""
+    desc, q, k, _ = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    g, _, _, s_ref = oracle_select(name)
+    _, inp1 = host_inputs(name, seed=1)
+    _, _, s1 = oracle.select(g, li.bf16_bits_to_f64(inp1.q), li.bf16_bits_to_f64(inp1.k))
+    tau = oracle.row_thresholds(g, s1)
+    rp, ci = lcsa.select_reuse(plan, q, k, torch.from_numpy(tau).cuda())
+    torch.cuda.synchronize()
+    pad = plan.info["max_window"]
+    rows_gpu = _check_padded(g, rp.cpu().numpy(), ci.cpu().numpy(), pad)
+    _compare_with_oracle(g, rows_gpu, s_ref, tau, name)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_reuse_with_own_thresholds_is_top_k(name):
+    desc, q, k, _ = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp0, ci0, kth, sc = lcsa.select_steady(plan, q, k, return_scores=True)
+    rp, ci = lcsa.select_reuse(plan, q, k, kth)
+    torch.cuda.synchronize()
+    g = oracle.geometry(desc)
+    pad = plan.info["max_window"]
+    rows_gpu = _check_padded(g, rp.cpu().numpy(), ci.cpu().numpy(), pad)
+    rp0_h, ci0_h, kth_h, sc_h = (x.cpu().numpy() for x in (rp0, ci0, kth, sc))
+    for (r, b, h, qb), a in zip(_rows(g), rows_gpu):
+        e = oracle.window(g, qb)
+        ties = int(np.sum(sc_h[b, h, qb, e] == kth_h[r]))
+        if ties == 1:
+            assert np.array_equal(a, ci0_h[rp0_h[r]:rp0_h[r + 1]]), f"row {r}"
+
+
+def test_reuse_extreme_thresholds():
+    desc, q, k, v = device_qkv("small_edges")
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    rows, pad = plan.info["rows"], plan.info["max_window"]
+    for label, val in (("-inf", -np.inf), ("+inf", np.inf), ("nan", np.nan)):
+        tau = torch.full((rows,), val, dtype=torch.float64, device="cuda")
+        rp, ci = lcsa.select_reuse(plan, q, k, tau)
+        o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+        torch.cuda.synchronize()
+        got = _check_padded(g, rp.cpu().numpy(), ci.cpu().numpy(), pad)
+        for (r, b, h, qb), a in zip(_rows(g), got):
+            want = oracle.window(g, qb) if val == -np.inf else np.empty(0, dtype=np.int64)
+            assert np.array_equal(a, want), f"tau {label} row {r}"
+        if val != -np.inf:   # nothing kept: O = 0, LSE = -inf
+            assert not torch.any(o.float() != 0) and bool(torch.all(torch.isneginf(lse)))
+        say(f"  tau {label}: ok")
+
+
+@pytest.mark.parametrize("name", SMALL + ["stream_768x1280"])
+def test_attend_on_padded_csr(name):
+    """Padded rows give bitwise the result of the same blocks compacted
+    (with and without the split tail), and match the oracle's attention."""
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    _, inp1 = host_inputs(name, seed=1)
+    _, _, s1 = oracle.select(g, li.bf16_bits_to_f64(inp1.q), li.bf16_bits_to_f64(inp1.k))
+    # a spread of row lengths: the other chunk's thresholds, raised on some rows
+    tau = oracle.row_thresholds(g, s1)
+    tau[::7] = np.inf
+    rp, ci = lcsa.select_reuse(plan, q, k, torch.from_numpy(tau).cuda())
+    ci_h = ci.cpu().numpy()
+    pad = plan.info["max_window"]
+    rows = _check_padded(g, rp.cpu().numpy(), ci_h, pad)
+    rp_c = np.concatenate([[0], np.cumsum([len(a) for a in rows])]).astype(np.int32)
+    ci_c = np.concatenate(rows + [np.empty(0, np.int32)]).astype(np.int32)
+    rp_cd = torch.from_numpy(rp_c).cuda()
+    ci_cd = torch.from_numpy(ci_c if len(ci_c) else np.zeros(1, np.int32)).cuda()[:len(ci_c)]
+    for split in (True, False):
+        o_p, lse_p = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True, split_tail=split)
+        o_c, lse_c = lcsa.attend(plan, q, k, v, rp_cd, ci_cd, return_lse=True, split_tail=split)
+        torch.cuda.synchronize()
+        assert torch.equal(o_p, o_c) and torch.equal(lse_p, lse_c), f"split_tail={split}"
+    if name in SMALL:
+        _, inp = host_inputs(name)
+        o_ref, lse_ref = oracle.attend(g, li.bf16_bits_to_f32(inp.q), li.bf16_bits_to_f32(inp.k),
+                                       li.bf16_bits_to_f32(inp.v), rp.cpu().numpy().astype(np.int64),
+                                       ci_h.astype(np.int64))
+        compare_output(bf16_to_np(o_p), o_ref, f"{name} padded CSR vs oracle")
+        lse_h = lse_p.cpu().numpy()
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isneginf(lse_h), np.isneginf(lse_ref))
+        assert float(np.abs(lse_h[fin] - lse_ref[fin]).max(initial=0.0)) <= 2e-3
+
+
+def test_ring_and_rope_forms_match():
+    """The ring and rotary forms of both calls give the plain forms' results."""
+    name = "small_edges"
+    desc, q, k, _ = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    kvf = plan.info["kv_frames"]
+    ft = desc["grid_h"] * desc["grid_w"]
+    slots = kvf + 1
+    frame_slot = [(t + 2) % slots for t in range(kvf)]
+    ring = lcsa.kv_ring(slots, frame_slot)
+    k_ring = torch.zeros((k.shape[0], slots * ft, k.shape[2], k.shape[3]), dtype=k.dtype,
+                         device=k.device)
+    for t, s in enumerate(frame_slot):
+        k_ring[:, s * ft:(s + 1) * ft] = k[:, t * ft:(t + 1) * ft]
+    kcache = torch.empty(lcsa.kcache_bytes(plan, slots) // 8, dtype=torch.float64, device="cuda")
+    rp0, ci0, kth0 = lcsa.select_steady(plan, q, k)
+    rp1, ci1, kth1 = lcsa.select_steady(plan, q, k_ring, ring=ring, new_frames=kvf, kcache=kcache)
+    tau = kth0 * 1.0001 - 1e-3
+    rq0, cq0 = lcsa.select_reuse(plan, q, k, tau)
+    rq1, cq1 = lcsa.select_reuse(plan, q, k_ring, tau, ring=ring, new_frames=0, kcache=kcache)
+    torch.cuda.synchronize()
+    assert torch.equal(rp0, rp1) and torch.equal(ci0, ci1) and torch.equal(kth0, kth1)
+    assert torch.equal(rq0, rq1) and torch.equal(cq0, cq1)
+
+    tabs = li.rope_tables(desc)
+    tt, th, tw = (torch.from_numpy(tabs[a]).cuda() for a in "thw")
+    tables = lcsa.rope(tt, th, tw)
+    q_rot0, k_rot0, rp2, ci2 = lcsa.select_rope(plan, q, k, tables)
+    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
+    rp3, ci3, kth3 = lcsa.select_steady(plan, q, k, tables=tables, q_rot=q_rot, k_rot=k_rot)
+    rq3, cq3 = lcsa.select_reuse(plan, q, k, kth3, tables=tables, q_rot=q_rot, k_rot=k_rot)
+    rq4, cq4 = lcsa.select_reuse(plan, q_rot0, k_rot0, kth3)
+    torch.cuda.synchronize()
+    assert torch.equal(q_rot, q_rot0) and torch.equal(k_rot, k_rot0)
+    assert torch.equal(rp3, rp2) and torch.equal(ci3, ci2)
+    assert torch.equal(rq3, rq4) and torch.equal(cq3, cq4)

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lcsa.abi_version() == 4
+    assert lcsa.abi_version() == 5
     lib = ctypes.CDLL(lcsa.lib_path())
     lib.lcsa_status_string.restype = ctypes.c_char_p
     texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
@@ -263,3 +263,35 @@ def test_plan_collected_at_interpreter_exit_is_quiet():
                        cwd=ROOT, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "Exception ignored" not in r.stderr, r.stderr
+
+
+def test_threshold_entry_point_validation_statuses():
+    """Arguments of the steady-threshold calls are checked on the host before
+    any HIP call; the ring and the rotary tables are each optional."""
+    p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])
+    good = _fake_view()
+    lib = lcsa._lib
+    ws, wsb = 0x40000, p.info["select_workspace_bytes"]
+    ok_ring = lcsa.kv_ring(4, [3, 0, 1])
+
+    def steady(kth=0x90000, ring=None, new=1, kc=0x80000, rope=None):
+        rg = ctypes.byref(ring) if ring is not None else None
+        rp = ctypes.byref(rope) if rope is not None else None
+        return lib.lcsa_select_steady(p.handle, ctypes.byref(good), ctypes.byref(good), rg, new,
+                                      kc, rp, ctypes.byref(good), ctypes.byref(good), 0x20000,
+                                      0x30000, kth, None, ws, wsb, None)
+
+    def reuse(tau=0x90000, ring=None, new=1, kc=0x80000):
+        rg = ctypes.byref(ring) if ring is not None else None
+        return lib.lcsa_select_reuse(p.handle, ctypes.byref(good), ctypes.byref(good), rg, new, kc,
+                                     None, None, None, tau, 0x20000, 0x30000, None, ws, wsb, None)
+    assert steady(kth=0) == 1 and reuse(tau=0) == 1                  # NULL thresholds
+    assert steady(kth=0x90004) == 4 and reuse(tau=0x90004) == 4      # ALIGN thresholds
+    assert steady(ring=lcsa.kv_ring(4, [3, 4, 1])) == 2              # ring checked when given
+    assert reuse(ring=ok_ring, new=9) == 2
+    assert reuse(ring=ok_ring, kc=0) == 1 and reuse(ring=ok_ring, kc=0x80008) == 4
+    bad_rope = lcsa.LcsaRope(pairs_t=23, pairs_h=21, pairs_w=21, reserved=0, table_t=0x50000,
+                             table_h=0x60000, table_w=0x70000)
+    assert steady(rope=bad_rope) == 2                                # rope checked when given
+    if not torch.cuda.is_available():
+        assert steady() == 6 and reuse() == 6 and reuse(ring=ok_ring) == 6   # DEVICE
