@@ -1,7 +1,7 @@
 """Planted mistakes in the oracle, on the CPU: each mutant below is a copy of
 the oracle with one plausible error (a dropped term, a wrong sign, index or
 bound, a transposed or swapped operand).  The pin suites (test_oracle.py,
-test_oracle_rope.py) must fail on every one of them, and pass on an
+test_oracle_rope.py, test_oracle_threshold.py) must fail on every one of them, and pass on an
 unmodified copy, which shows the pins constrain each part of the oracle and
 that the copy is the module the suites import."""
 import os
@@ -12,7 +12,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_SUITES = [os.path.join(ROOT, "tests", "test_oracle.py"),
-              os.path.join(ROOT, "tests", "test_oracle_rope.py")]
+              os.path.join(ROOT, "tests", "test_oracle_rope.py"),
+              os.path.join(ROOT, "tests", "test_oracle_threshold.py")]
 
 # (name, original text, planted text) in oracle/lcsa_oracle.py
 MUTANTS = [
@@ -47,6 +48,21 @@ ROPE_MUTANTS = [
 ]
 
 
+# the same in oracle/threshold_oracle.py
+THRESHOLD_MUTANTS = [
+    ("threshold_strict", "out.append(e[s[b, h, qb, e] >= tau[r]])", "out.append(e[s[b, h, qb, e] > tau[r]])"),
+    ("threshold_one_past_keep", "np.sort(s[b, h, qb, e])[::-1][keep - 1]",
+     "np.sort(s[b, h, qb, e])[::-1][min(keep, len(e) - 1)]"),
+    ("threshold_smallest_instead", "np.sort(s[b, h, qb, e])[::-1][keep - 1]", "np.sort(s[b, h, qb, e])[keep - 1]"),
+    ("threshold_whole_row", "out.append(e[s[b, h, qb, e] >= tau[r]])",
+     "out.append(np.flatnonzero(s[b, h, qb] >= tau[r]))"),
+    ("threshold_padding_zero", "col_idx = np.full(len(rows) * w, -1, dtype=np.int64)",
+     "col_idx = np.full(len(rows) * w, 0, dtype=np.int64)"),
+    ("threshold_row_order_swapped", "yield (b * g.heads + h) * g.nqb + qb, b, h, qb",
+     "yield (h * g.batch + b) * g.nqb + qb, b, h, qb"),
+]
+
+
 def _run_suite(tmp, name, fname, old, new):
     d = os.path.join(tmp, name)
     shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(d, "oracle"),
@@ -67,7 +83,8 @@ def _run_suite(tmp, name, fname, old, new):
 def test_pins_fail_on_every_planted_mistake(tmp_path):
     jobs = ([("control", None, None, None)]
             + [(n, "lcsa_oracle.py", a, b) for n, a, b in MUTANTS]
-            + [(n, "rope_oracle.py", a, b) for n, a, b in ROPE_MUTANTS])
+            + [(n, "rope_oracle.py", a, b) for n, a, b in ROPE_MUTANTS]
+            + [(n, "threshold_oracle.py", a, b) for n, a, b in THRESHOLD_MUTANTS])
     with ThreadPoolExecutor(max_workers=6) as pool:
         results = list(pool.map(lambda j: _run_suite(str(tmp_path), *j), jobs))
     control = results[0]

@@ -5,13 +5,16 @@ thresholds are the keep-th largest window scores (brute force over the
 sorted window on a tiny grid); the padded layout holds each row's blocks
 first.  CPU only."""
 import numpy as np
+import pytest
 
 import lcsa_inputs as li
 import oracle
 
 
-def _scores(name, seed=0):
+def _scores(name, seed=0, batch=None):
     desc = dict(li.CONFIGS[name])
+    if batch is not None:
+        desc["batch"] = batch
     g = oracle.geometry(desc)
     inp = li.generate(desc, seed=seed)
     q, k = li.bf16_bits_to_f64(inp.q), li.bf16_bits_to_f64(inp.k)
@@ -20,16 +23,20 @@ def _scores(name, seed=0):
 
 
 def test_own_thresholds_reproduce_top_k():
-    for name in ("tiny", "tiny_window", "small_edges", "small_16x8"):
-        g, rp, ci, s = _scores(name)
+    for name, batch in (("tiny", None), ("tiny_window", None), ("small_edges", None),
+                        ("small_16x8", None), ("tiny", 2)):
+        g, rp, ci, s = _scores(name, batch=batch)
         tau = oracle.row_thresholds(g, s)
         rows = oracle.select_threshold(g, s, tau)
         for r, blocks in enumerate(rows):
             assert np.array_equal(blocks, ci[rp[r]:rp[r + 1]]), f"{name} row {r}"
 
 
-def test_thresholds_are_kth_scores_by_brute_force():
-    g, rp, ci, s = _scores("tiny_window")
+@pytest.mark.parametrize("name,batch", [("tiny_window", None), ("tiny", 2)])
+def test_thresholds_are_kth_scores_by_brute_force(name, batch):
+    # thresholds are indexed by CSR row (b, h, query block); batch 2 tells
+    # that order from (h, b, query block)
+    g, rp, ci, s = _scores(name, batch=batch)
     tau = oracle.row_thresholds(g, s)
     for r in range(len(rp) - 1):
         b, rem = divmod(r, g.heads * g.nqb)
