@@ -167,11 +167,22 @@ def test_attend_on_padded_csr(name):
     ci_c = np.concatenate(rows + [np.empty(0, np.int32)]).astype(np.int32)
     rp_cd = torch.from_numpy(rp_c).cuda()
     ci_cd = torch.from_numpy(ci_c if len(ci_c) else np.zeros(1, np.int32)).cuda()[:len(ci_c)]
+    res = {}
     for split in (True, False):
         o_p, lse_p = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True, split_tail=split)
         o_c, lse_c = lcsa.attend(plan, q, k, v, rp_cd, ci_cd, return_lse=True, split_tail=split)
         torch.cuda.synchronize()
         assert torch.equal(o_p, o_c) and torch.equal(lse_p, lse_c), f"split_tail={split}"
+        res[split] = (o_p, lse_p)
+    # with the workspace the rows of the last partly filled round run as
+    # merged pieces: the same result to rounding
+    d = float((res[True][0].float() - res[False][0].float()).abs().max())
+    fin = torch.isfinite(res[False][1])
+    assert torch.equal(fin, torch.isfinite(res[True][1]))
+    dl = float((res[True][1][fin] - res[False][1][fin]).abs().max()) if bool(fin.any()) else 0.0
+    say(f"  {name}: split tail vs whole rows: O max|d| {d:.3e}, LSE max|d| {dl:.3e}")
+    assert d <= 1e-2 and dl <= 2e-3   # P is rounded to bf16 against each piece's own reference
+    o_p, lse_p = res[True]
     if name in SMALL:
         _, inp = host_inputs(name)
         o_ref, lse_ref = oracle.attend(g, li.bf16_bits_to_f32(inp.q), li.bf16_bits_to_f32(inp.k),
