@@ -74,7 +74,11 @@ def _run_suite(tmp, name, fname, old, new):
     env = dict(os.environ, PYTHONPATH=os.pathsep.join([d, ROOT]), OMP_NUM_THREADS="2")
     # run from the copy's directory: `python -m` puts the working directory
     # first on sys.path, so the copy shadows the repository's oracle
-    r = subprocess.run([sys.executable, "-m", "pytest", *PIN_SUITES,
+    # the suite of the mutated module first: with -x a caught mutant stops
+    # at its first failing pin instead of after the other suites pass
+    own = {"rope_oracle.py": 1, "threshold_oracle.py": 2}.get(fname, 0)
+    suites = [PIN_SUITES[own]] + [x for i, x in enumerate(PIN_SUITES) if i != own]
+    r = subprocess.run([sys.executable, "-m", "pytest", *suites,
                         "-x", "-q", "-p", "no:cacheprovider", "--rootdir", ROOT], cwd=d, env=env,
                        capture_output=True, text=True, timeout=900)
     return name, r.returncode, (r.stdout + r.stderr)[-600:]
