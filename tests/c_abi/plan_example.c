@@ -74,6 +74,14 @@ int main(int argc, char** argv) {
   printf("\n");
   free(win);
   printf("status_string %s\n", lcsa_status_string(LCSA_ERR_SHAPE));
+  /* threshold calls reject a missing threshold array on the host, before any
+     HIP call */
+  st = lcsa_select_reuse(plan, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                         NULL, NULL, 0, NULL);
+  printf("reuse_without_tau %d\n", (int)st);
+  st = lcsa_select_steady(plan, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                          NULL, NULL, 0, NULL);
+  printf("steady_without_kth %d\n", (int)st);
   lcsa_plan_destroy(plan);
   lcsa_plan_destroy(NULL);
   return 0;

@@ -63,6 +63,7 @@ def test_c_program_plans_match_oracle(program, name):
     assert int(out["row_ptr_hash"]) == h
     assert [int(x) for x in out["window0"].split()] == oracle.window(g, 0).tolist()
     assert out["status_string"].strip() != ""
+    assert int(out["reuse_without_tau"]) == 1 and int(out["steady_without_kth"]) == 1   # NULL
 
 
 def test_c_program_reports_errors(program):
