@@ -65,3 +65,42 @@ def test_select_template_parity(label, desc, m_want, r_want):
     assert float(np.abs(s_gpu[fin] - s_ref[fin]).max()) <= 1e-12 * float(np.abs(s_ref[fin]).max())
     mism, ties = check_mask(g, rp_ref, ci_ref, s_ref, rp.cpu().numpy(), ci.cpu().numpy())
     say(f"  mask mismatches {len(mism)}, all near-ties ({len(ties)})")
+
+
+@pytest.mark.parametrize("label,desc,m_want,r_want", CASES, ids=[c[0] for c in CASES])
+def test_threshold_modes_every_template(label, desc, m_want, r_want):
+    """The k-th score output and the threshold selection in every compiled
+    width: steady thresholds equal the oracle's (1e-12 of the score scale),
+    and thresholds of another chunk (seed 4) select exactly the oracle's
+    blocks except within 1e-9 of the scale of a threshold, padded with -1."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    plan = lcsa.Plan.from_desc(desc)
+    info = plan.info
+    say(f"[gpu] threshold modes {label}: window {info['min_window']}..{info['max_window']}")
+    g = oracle.geometry(desc)
+    inp = li.generate(desc, seed=3)
+    q, k = to_device_bf16(inp.q), to_device_bf16(inp.k)
+    _, _, s_ref = oracle.select(g, li.bf16_bits_to_f64(inp.q), li.bf16_bits_to_f64(inp.k))
+    inp1 = li.generate(desc, seed=4)
+    _, _, s1 = oracle.select(g, li.bf16_bits_to_f64(inp1.q), li.bf16_bits_to_f64(inp1.k))
+    _, _, kth = lcsa.select_steady(plan, q, k)
+    tau = oracle.row_thresholds(g, s1)
+    rp, ci = lcsa.select_reuse(plan, q, k, torch.from_numpy(tau).cuda())
+    torch.cuda.synchronize()
+    scale = float(np.abs(s_ref[np.isfinite(s_ref)]).max())
+    assert float(np.abs(kth.cpu().numpy() - oracle.row_thresholds(g, s_ref)).max()) <= 1e-12 * scale
+    pad = info["max_window"]
+    rows_ref = oracle.select_threshold(g, s_ref, tau)
+    rp_ref, ci_ref = oracle.padded_csr(g, rows_ref)
+    assert np.array_equal(rp.cpu().numpy(), rp_ref)
+    ci_h = ci.cpu().numpy().astype(np.int64)
+    for r, want in enumerate(rows_ref):
+        seg = ci_h[r * pad:(r + 1) * pad]
+        got = seg[seg >= 0]
+        assert np.all(seg[len(got):] == -1)
+        if not np.array_equal(got, want):
+            b, rem = divmod(r, g.heads * g.nqb)
+            h, qb = divmod(rem, g.nqb)
+            for kb in set(got.tolist()) ^ set(want.tolist()):
+                assert abs(s_ref[b, h, qb, kb] - tau[r]) <= 1e-9 * scale, f"{label} row {r}"
