@@ -62,3 +62,49 @@ def test_random_config_parity(case):
     compare_output(bf16_to_np(o), o_ref, f"random case {case}")
     lse_h = lse.cpu().numpy()
     assert np.all(np.abs(lse_h - lse_ref) <= 2e-3 * np.maximum(1.0, np.abs(lse_ref)))
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_random_config_threshold_reuse(case):
+    """Threshold reuse on the same random configurations: the oracle's
+    thresholds of another chunk (seed + 100) select exactly the oracle's
+    blocks (up to 1e-9 of the score scale of a threshold), and attention on
+    the padded CSR meets the parity bar against the oracle on that mask."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    desc = CASES[case]
+    plan = lcsa.Plan.from_desc(desc)
+    info = plan.info
+    say(f"[gpu] random reuse case {case}: window {info['min_window']}..{info['max_window']}, "
+        f"rows {info['rows']}")
+    g = oracle.geometry(desc)
+    inp = li.generate(desc, seed=case)
+    inp1 = li.generate(desc, seed=case + 100)
+    qf, kf, vf = (li.bf16_bits_to_f64(x) for x in (inp.q, inp.k, inp.v))
+    _, _, s_ref = oracle.select(g, qf, kf)
+    _, _, s1 = oracle.select(g, li.bf16_bits_to_f64(inp1.q), li.bf16_bits_to_f64(inp1.k))
+    tau = oracle.row_thresholds(g, s1)
+    q, k, v = (to_device_bf16(x) for x in (inp.q, inp.k, inp.v))
+    rp, ci = lcsa.select_reuse(plan, q, k, torch.from_numpy(tau).cuda())
+    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+    torch.cuda.synchronize()
+    pad = info["max_window"]
+    rows_ref = oracle.select_threshold(g, s_ref, tau)
+    rp_h, ci_h = rp.cpu().numpy().astype(np.int64), ci.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp_h, np.arange(info["rows"] + 1) * pad)
+    scale = float(np.abs(s_ref[np.isfinite(s_ref)]).max())
+    for r, want in enumerate(rows_ref):
+        seg = ci_h[r * pad:(r + 1) * pad]
+        got = seg[seg >= 0]
+        assert np.all(seg[len(got):] == -1) and np.all(np.diff(got) > 0)
+        if not np.array_equal(got, want):
+            b, rem = divmod(r, g.heads * g.nqb)
+            h, qb = divmod(rem, g.nqb)
+            for kb in set(got.tolist()) ^ set(want.tolist()):
+                assert abs(s_ref[b, h, qb, kb] - tau[r]) <= 1e-9 * scale, f"case {case} row {r}"
+    o_ref, lse_ref = oracle.attend(g, qf, kf, vf, rp_h, ci_h)
+    compare_output(bf16_to_np(o), o_ref, f"random reuse case {case}")
+    lse_h = lse.cpu().numpy()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isneginf(lse_h), np.isneginf(lse_ref))
+    assert np.all(np.abs(lse_h[fin] - lse_ref[fin]) <= 2e-3 * np.maximum(1.0, np.abs(lse_ref[fin])))
