@@ -284,3 +284,40 @@ def test_threshold_chain_in_graph():
             assert torch.equal(a, b), f"replay {rep}: {what} differs from eager"
         say(f"  replay {rep} (seed {seed}): bitwise equal to eager")
     del g
+
+
+def test_ring_rope_steady_matches_ring_rope_select():
+    """Ring and rotary tables together: lcsa_select_steady gives the CSR and
+    turned tensors of lcsa_select_ring_rope bit for bit."""
+    name = "small_edges"
+    desc, q, k, _ = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    kvf = plan.info["kv_frames"]
+    ft = desc["grid_h"] * desc["grid_w"]
+    slots = kvf + 2
+    frame_slot = [(t + 3) % slots for t in range(kvf)]
+    ring = lcsa.kv_ring(slots, frame_slot)
+    k_ring = torch.zeros((k.shape[0], slots * ft, k.shape[2], k.shape[3]), dtype=k.dtype,
+                         device=k.device)
+    for t, s in enumerate(frame_slot):
+        k_ring[:, s * ft:(s + 1) * ft] = k[:, t * ft:(t + 1) * ft]
+    tabs = li.rope_tables(desc)
+    tables = lcsa.rope(*(torch.from_numpy(tabs[a]).cuda() for a in "thw"))
+    kc1 = torch.empty(lcsa.kcache_bytes(plan, slots) // 8, dtype=torch.float64, device="cuda")
+    kc2 = torch.empty_like(kc1)
+    kr1, kr2 = torch.zeros_like(k_ring), torch.zeros_like(k_ring)
+    q_rot1, rp1, ci1 = lcsa.select_ring_rope(plan, q, k_ring, ring, kvf, kc1, tables, kr1)
+    q_rot2 = torch.empty_like(q)
+    rp2, ci2, kth2 = lcsa.select_steady(plan, q, k_ring, ring=ring, new_frames=kvf, kcache=kc2,
+                                        tables=tables, q_rot=q_rot2, k_rot=kr2)
+    rq, cq = lcsa.select_reuse(plan, q, k_ring, kth2, ring=ring, new_frames=kvf, kcache=kc2,
+                               tables=tables, q_rot=q_rot2, k_rot=kr2)
+    torch.cuda.synchronize()
+    assert torch.equal(q_rot1, q_rot2) and torch.equal(kr1, kr2)
+    assert torch.equal(rp1, rp2) and torch.equal(ci1, ci2)
+    used = torch.tensor(frame_slot, device="cuda")   # the other slots hold no frame
+    assert torch.equal(kc1.view(slots, -1)[used], kc2.view(slots, -1)[used])
+    g = oracle.geometry(desc)
+    rows = _check_padded(g, rq.cpu().numpy(), cq.cpu().numpy(), plan.info["max_window"])
+    say(f"  ring + rope: steady equals ring rotary select; reuse kept {sum(len(r) for r in rows)} "
+        f"blocks against {int(rp1[-1])} top-k")
