@@ -309,9 +309,9 @@ lcsa_status lcsa_select_ring_rope(lcsa_plan_t plan, const lcsa_tensor* q,
                                   int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
                                   void* d_workspace, size_t workspace_bytes, void* stream);
 
-/* Steady threshold reuse.  The final GH200 configuration of the FlashVSR
- * Hopper PR page keeps, per DiT block, the mask threshold of a steady chunk
- * and reuses it for later chunks instead of ranking the scores again
+/* Steady threshold reuse.  On the FlashVSR Hopper PR page the last GH200
+ * configuration stores each DiT block's mask threshold from a steady chunk
+ * and applies it to later chunks in place of a new ranking
  * ("Remove the remaining control-plane tax"; quality-gated in "Recommended
  * GH200 Controls").  The page does not define the threshold; here it is
  * each CSR row's keep-th largest window score (keep = min(k, |window|)),

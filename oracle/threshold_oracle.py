@@ -5,10 +5,11 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
 this module; only the tests, the smoke check and the bench's CPU-baseline leg
 do.  It shares no code with the HIP library.
 
-What the pages state: the final GH200 set adds a steady mask-threshold cache
-(FlashVSR Hopper PR page, "Remove the remaining control-plane tax"), which
-reuses the previous steady chunk's threshold per DiT block and is
-quality-gated ("Recommended GH200 Controls").
+What the pages state: among the last GH200 optimisations is a cache of mask
+thresholds (FlashVSR Hopper PR page, "Remove the remaining control-plane
+tax"): each DiT block keeps the threshold found on a steady chunk and uses it
+again on the next one, a switch that is accepted only on quality
+("Recommended GH200 Controls").
 
 The pages do not define the threshold or its use.  Reading taken here (R11,
 listed with the others in the design notes):
