@@ -28,8 +28,9 @@
 // row share (found from a wave-wide OR and AND) need no count.
 //
 // Steady threshold reuse (FlashVSR Hopper PR page, "Remove the remaining
-// control-plane tax" and "Recommended GH200 Controls": a steady chunk's
-// mask threshold is kept per DiT block and reused): the top-k run can also
+// control-plane tax" and "Recommended GH200 Controls": each DiT block holds
+// on to the mask threshold of a steady chunk for the chunks after it): the
+// top-k run can also
 // write each row's keep-th largest window score, and a threshold run keeps,
 // instead of the top-k, every window block scored at or above its row's
 // given threshold.  Threshold rows vary in length, so they are written at a
