@@ -272,6 +272,42 @@ def test_attend_equals_token_masked_sdpa(name, batch):
             np.testing.assert_allclose(lse[b, h], logsumexp(z, axis=1), rtol=1e-12)
 
 
+@pytest.mark.parametrize("name", ["tiny_window", "small_edges"])
+def test_attend_rows_equals_attend_on_every_row(name):
+    """attend_rows decodes each CSR row r into (batch, head, query block) on
+    its own; on batch-2, multi-head grids (where any other decode order
+    names different tokens) it must give attend's O and LSE bit for bit on
+    every row, asked for in a shuffled order with repeats, and a sample of
+    its rows must equal the token-masked SDPA of that row."""
+    desc = _desc(name, batch=2, heads=3)
+    g = oracle.geometry(desc)
+    q, k, v = _rand_inputs(desc, 41)
+    rp, ci, _ = oracle.select(g, q, k)
+    o, lse = oracle.attend(g, q, k, v, rp, ci)
+    rows = g.batch * g.heads * g.nqb
+    order = np.random.default_rng(2).permutation(rows).tolist() + [0, rows - 1, rows // 2]
+    got = oracle.attend_rows(g, q, k, v, rp, ci, order)
+    assert len(got) == len(order)
+    seen = set()
+    for r, (b, h, qtok, orow, lrow) in zip(order, got):
+        qb = r % g.nqb
+        assert (b, h) == divmod(r // g.nqb, g.heads)
+        assert np.array_equal(qtok, oracle.block_tokens(g, qb))
+        assert np.array_equal(orow, o[b, qtok, h]) and np.array_equal(lrow, lse[b, h, qtok])
+        seen.add(r)
+    assert seen == set(range(rows))
+    qid = _token_block_ids(g, g.q_frames)
+    kid = _token_block_ids(g, g.kv_frames)
+    for r in [1, rows // 3, rows - 2]:
+        b, h, qtok, orow, _ = oracle.attend_rows(g, q, k, v, rp, ci, [r])[0]
+        allowed = np.zeros(g.nkb, dtype=bool)
+        allowed[ci[rp[r]:rp[r + 1]]] = True
+        qsel = qid == r % g.nqb
+        ref = _sdpa(q[b, :, h], k[b, :, h], v[b, :, h], mask=np.broadcast_to(
+            allowed[kid], (g.q_tokens, g.kv_tokens)).copy())[qsel]
+        np.testing.assert_allclose(orow, ref, rtol=1e-11, atol=1e-12)
+
+
 def test_attend_row_stochastic_and_bounded():
     desc = li.CONFIGS["small_edges"]
     g = oracle.geometry(desc)

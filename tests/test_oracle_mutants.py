@@ -34,6 +34,10 @@ MUTANTS = [
     ("attend_lse_without_log", "lse = m[:, 0] + np.log(den[:, 0])", "lse = m[:, 0] + den[:, 0]"),
     ("attend_row_head_swap", "r = (b * g.heads + h) * g.nqb + qb", "r = (h * g.batch + b) * g.nqb + qb"),
     ("flops_half", "return 4.0 * g.head_dim", "return 2.0 * g.head_dim"),
+    ("attend_rows_head_block_swapped", "        h, qb = divmod(rem, g.nqb)\n        blocks",
+     "        qb, h = divmod(rem, g.heads)\n        blocks"),
+    ("attend_rows_batch_stride", "b, rem = divmod(int(r), g.heads * g.nqb)",
+     "b, rem = divmod(int(r), g.batch * g.nqb)"),
 ]
 
 # the same in oracle/rope_oracle.py
