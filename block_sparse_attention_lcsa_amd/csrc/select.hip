@@ -42,6 +42,7 @@
 #include "kernel_params.h"
 #include "launch.h"
 #include "lcsa_internal.h"
+#include "topk_wave.h"
 
 namespace lcsa {
 namespace {
@@ -210,24 +211,18 @@ __device__ inline int window_kb(const GridGeom& g, const WindowBox& w, int e) {
   return t * g.nbf + (w.y0 + yy) * g.nbw + (w.x0 + xx);
 }
 
-// Order-preserving key of a double (larger score -> larger key; -0 == +0).
-__device__ inline uint64_t order_key(double s) {
-  const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-__device__ inline int wave_count(bool pred) {
-  return __popcll(__builtin_amdgcn_ballot_w64(pred));
-}
-
-// Wave-wide OR and AND of a 64-bit value.
-__device__ inline void wave_or_and(uint64_t& o, uint64_t& a) {
+// The wave's cross-lane operations for the top-k of topk_wave.h.
+struct DeviceWave {
+  __device__ uint64_t ballot(bool pred) const { return __builtin_amdgcn_ballot_w64(pred); }
+  // wave-wide OR and AND of a 64-bit value
+  __device__ void or_and(uint64_t& o, uint64_t& a) const {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    o |= (uint64_t)__shfl_xor((unsigned long long)o, m);
-    a &= (uint64_t)__shfl_xor((unsigned long long)a, m);
+    for (int m = 32; m >= 1; m >>= 1) {
+      o |= (uint64_t)__shfl_xor((unsigned long long)o, m);
+      a &= (uint64_t)__shfl_xor((unsigned long long)a, m);
+    }
   }
-}
+};
 
 // One workgroup takes the rows of up to R query frames at one spatial
 // position; they share the window.  Scores: wave w computes window
@@ -344,6 +339,7 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   }
   const int keep = min(g.k, w.n);
   const uint64_t below = (1ull << lane) - 1ull;
+  DeviceWave dw;
   int kb[M];
   bool valid[M];
 #pragma unroll
@@ -402,51 +398,9 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
       for (int j = 0; j < M; ++j) sel[j] = valid[j];
     } else {
       uint64_t key[M];
-      uint64_t kor = 0ull, kand = ~0ull;
 #pragma unroll
-      for (int j = 0; j < M; ++j) {
-        key[j] = valid[j] ? order_key(s[j]) : 0ull;
-        kor |= valid[j] ? key[j] : 0ull;
-        kand &= valid[j] ? key[j] : ~0ull;
-      }
-      wave_or_and(kor, kand);
-      // Every valid key shares the bits above the highest bit where two of
-      // them differ, so the bisection starts there.  Largest T with
-      // #{key >= T} >= keep, decided bit by bit from the top.  Invalid lanes
-      // hold key 0, which never reaches a trial value > 0.
-      const uint64_t diff = kor ^ kand;
-      const int hb = diff ? 63 - __clzll(diff) : -1;
-      uint64_t t = hb >= 63 ? 0ull : kand & ~((2ull << hb) - 1ull);
-      bool exact = false;
-      for (int bit = hb; bit >= 0; --bit) {
-        const uint64_t trial = t | (1ull << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < M; ++j) cnt += wave_count(key[j] >= trial);
-        if (cnt >= keep) t = trial;
-        if (cnt == keep) {  // the set {key >= trial} is exactly the top keep
-          exact = true;
-          break;
-        }
-      }
-      if (exact) {
-#pragma unroll
-        for (int j = 0; j < M; ++j) sel[j] = valid[j] && key[j] >= t;
-      } else {
-        // t is the keep-th largest key; keys == t are admitted by index.
-        int need = keep;
-#pragma unroll
-        for (int j = 0; j < M; ++j) need -= wave_count(valid[j] && key[j] > t);
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-          const bool tie = valid[j] && key[j] == t;
-          const uint64_t tm = __builtin_amdgcn_ballot_w64(tie);
-          const int rank = __popcll(tm & below);
-          sel[j] = (valid[j] && key[j] > t) || (tie && rank < need);
-          need -= __popcll(tm);
-          need = need < 0 ? 0 : need;
-        }
-      }
+      for (int j = 0; j < M; ++j) key[j] = valid[j] ? order_key(s[j]) : 0ull;
+      topk_select<M>(dw, lane, key, valid, keep, sel);
     }
 
     if (p.kth) {  // the smallest kept score is the keep-th largest
@@ -458,14 +412,13 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
       if (lane == 0) p.kth[row] = mn;
     }
 
-    // Emit kept blocks in ascending candidate (= key block) order.
-    int base = 0;
+    // Emit kept blocks in ascending candidate (= key block) order; a row
+    // writes at most its own keep entries.
+    int at[M];
+    kept_positions<M>(dw, lane, sel, keep, at);
 #pragma unroll
-    for (int j = 0; j < M; ++j) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64(sel[j]);
-      if (sel[j]) p.col_idx[off + base + __popcll(m & below)] = kb[j];
-      base += __popcll(m);
-    }
+    for (int j = 0; j < M; ++j)
+      if (at[j] >= 0) p.col_idx[off + at[j]] = kb[j];
   }
 }
 

@@ -1,0 +1,140 @@
+"""Exact ties in block selection, through the C ABI, against the oracle.
+
+Top-k keeps the k highest pooled scores of a row's window and gives equal
+scores to the lower block index (the mask selection and CSR construction of
+the FlashVSR Hopper PR page, "What Was Actually Slow" and "Rebuild sparse
+attention for Hopper"; the tie rule is reading R5).  Synthetic inputs almost
+never tie, so the ties here are built into the inputs, in ways that make the
+two sides' float64 scores tie exactly too:
+
+  zero_q     the query tokens of some query blocks are exactly 0, so every
+             score of those rows is exactly 0: the whole window ties;
+  dup_k      groups of 2 and 3 consecutive key blocks in turn hold the
+             tokens of the group's first block, so their pooled keys are
+             equal and rows see runs of equal scores, ties at the k-th score
+             among them;
+  const_k    every key token is the same vector: every row's window ties.
+
+The CSR must equal the oracle's exactly (no near-tie allowance: these ties
+are exact on both sides), for lcsa_select and lcsa_select_steady, and no
+entry of row_ptr or col_idx past its end may be written (both buffers carry
+a guard region of a sentinel value).  The steady call's thresholds are the
+keep-th largest window score, the tie value itself on tied rows."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import lcsa_inputs as li
+import oracle
+from gpu_util import say, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+import block_sparse_attention_lcsa_amd as lcsa  # noqa: E402  (fails loudly if not built)
+
+WORKLOADS = ["tiny", "tiny_window", "small_edges", "small_16x8", "stream_768x1280",
+             "first_768x1280"]
+MODES = ["zero_q", "dup_k", "const_k"]
+GUARD = 4096
+SENTINEL = 0x5A5A5A5A
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say(f"[gpu] start {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+    say(f"[gpu] done  {request.node.nodeid}")
+
+
+def _tied_inputs(name, mode):
+    desc = dict(li.CONFIGS[name])
+    inp = li.generate(desc, seed=7)
+    g = oracle.geometry(desc)
+    q, k = inp.q.copy(), inp.k.copy()
+    if mode == "zero_q":
+        # the first, a middle and the last query block: corner, interior, edge
+        for qb in sorted({0, g.nqb // 2 + g.nbw // 2, g.nqb - 1}):
+            q[:, oracle.block_tokens(g, qb)] = 0
+    elif mode == "dup_k":
+        # groups of 2 and 3 consecutive key blocks in turn share the first
+        # block's tokens, so group sizes do not line up with any one k
+        kb, size = 0, 2
+        while kb < g.nkb:
+            for j in range(kb + 1, min(kb + size, g.nkb)):
+                k[:, oracle.block_tokens(g, j)] = k[:, oracle.block_tokens(g, kb)]
+            kb, size = kb + size, 5 - size
+    else:
+        k[:] = li.f32_to_bf16_bits(np.float32(0.375))
+    return desc, g, q, k
+
+
+def _raw_select(plan, q, k, steady):
+    """lcsa_select / lcsa_select_steady into guard-padded CSR buffers."""
+    inf = plan.info
+    rows, nnz = int(inf["rows"]), int(inf["nnz"])
+    rp = torch.full((rows + 1 + GUARD,), SENTINEL, dtype=torch.int32, device="cuda")
+    ci = torch.full((nnz + GUARD,), SENTINEL, dtype=torch.int32, device="cuda")
+    kth = torch.full((rows + GUARD,), np.nan, dtype=torch.float64, device="cuda")
+    ws = torch.empty(max(int(inf["select_workspace_bytes"]), 256), dtype=torch.uint8,
+                     device="cuda")
+    qv, kv = lcsa.tensor_view(q), lcsa.tensor_view(k)
+    stream = torch.cuda.current_stream().cuda_stream
+    if steady:
+        st = lcsa._lib.lcsa_select_steady(plan.handle, ctypes.byref(qv), ctypes.byref(kv), None,
+                                          0, None, None, None, None, rp.data_ptr(),
+                                          ci.data_ptr(), kth.data_ptr(), None, ws.data_ptr(),
+                                          ws.numel(), stream)
+    else:
+        st = lcsa._lib.lcsa_select(plan.handle, ctypes.byref(qv), ctypes.byref(kv),
+                                   rp.data_ptr(), ci.data_ptr(), None, ws.data_ptr(),
+                                   ws.numel(), stream)
+    assert st == 0, lcsa._lib.lcsa_last_error().decode()
+    torch.cuda.synchronize()
+    rp_h, ci_h, kth_h = rp.cpu().numpy(), ci.cpu().numpy(), kth.cpu().numpy()
+    assert np.all(rp_h[rows + 1:] == SENTINEL), "row_ptr written past its end"
+    assert np.all(ci_h[nnz:] == SENTINEL), "col_idx written past its end"
+    if steady:
+        assert np.all(np.isnan(kth_h[rows:])), "thresholds written past their end"
+    return rp_h[:rows + 1], ci_h[:nnz], kth_h[:rows]
+
+
+def _tied_rows(g, s, rp):
+    """Rows whose k-th and (k+1)-th largest window scores are equal."""
+    n = 0
+    for r in range(len(rp) - 1):
+        b, rem = divmod(r, g.heads * g.nqb)
+        h, qb = divmod(rem, g.nqb)
+        e = oracle.window(g, qb)
+        keep = min(g.k, len(e))
+        if keep < len(e):
+            srt = np.sort(s[b, h, qb, e])[::-1]
+            n += int(srt[keep - 1] == srt[keep])
+    return n
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_exact_ties_match_oracle(name, mode):
+    desc, g, q_bits, k_bits = _tied_inputs(name, mode)
+    plan = lcsa.Plan.from_desc(desc)
+    q, k = to_device_bf16(q_bits), to_device_bf16(k_bits)
+    rp, ci, _ = _raw_select(plan, q, k, steady=False)
+    rp_s, ci_s, kth = _raw_select(plan, q, k, steady=True)
+    rp_ref, ci_ref, s_ref = oracle.select(g, li.bf16_bits_to_f64(q_bits),
+                                          li.bf16_bits_to_f64(k_bits))
+    tied = _tied_rows(g, s_ref, rp_ref)
+    say(f"  {name} {mode}: {tied} of {len(rp_ref) - 1} rows tie at the k-th score")
+    assert tied > 0, "the construction made no tie at the k-th score"
+    assert np.array_equal(rp.astype(np.int64), rp_ref)
+    bad = [r for r in range(len(rp_ref) - 1)
+           if not np.array_equal(ci[rp_ref[r]:rp_ref[r + 1]], ci_ref[rp_ref[r]:rp_ref[r + 1]])]
+    assert not bad, f"{len(bad)} rows differ from the oracle, first {bad[:5]}"
+    assert np.array_equal(rp_s, rp) and np.array_equal(ci_s, ci)
+    tau_ref = oracle.row_thresholds(g, s_ref)
+    scale = float(np.abs(s_ref[np.isfinite(s_ref)]).max()) or 1.0
+    assert float(np.abs(kth - tau_ref).max()) <= 1e-12 * scale
