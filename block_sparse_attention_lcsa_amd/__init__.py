@@ -72,7 +72,9 @@ class LcsaDesc(ctypes.Structure):
 class LcsaTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("stride_b", ctypes.c_int64),
-                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("batch", ctypes.c_int64), ("tokens", ctypes.c_int64),
+                ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64)]
 
 
 class LcsaKvRing(ctypes.Structure):
@@ -238,8 +240,10 @@ def tensor_view(t) -> LcsaTensor:
     if t.dim() != 4 or t.stride(3) != 1:
         raise ValueError("expected a [batch, tokens, heads, head_dim] view with contiguous last dim")
     sb, ss, sh, _ = t.stride()
+    nb, ns, nh, nd = t.shape
     return LcsaTensor(data=t.data_ptr(), dtype=LCSA_DTYPE_BF16, reserved=0,
-                      stride_b=sb, stride_s=ss, stride_h=sh)
+                      stride_b=sb, stride_s=ss, stride_h=sh, batch=nb, tokens=ns, heads=nh,
+                      head_dim=nd)
 
 
 def _check_shape(t, plan: Plan, tokens_key: str, name: str):

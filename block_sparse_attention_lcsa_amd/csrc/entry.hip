@@ -56,8 +56,10 @@ lcsa_status device_cus(int* out) {
   return LCSA_OK;
 }
 
-lcsa_status check_view(const char* name, const lcsa_tensor* t, int64_t tokens, int heads,
-                       bool allow_null_data = false) {
+// A view's pointer, dtype, alignment and strides, and its extents against
+// [batch, tokens, heads, 128] of the plan and call.
+lcsa_status check_view(const char* name, const lcsa_tensor* t, int batch, int64_t tokens,
+                       int heads, bool allow_null_data = false) {
   if (!t) return fail(LCSA_ERR_NULL, "%s: tensor descriptor is NULL", name);
   if (!t->data && !allow_null_data) return fail(LCSA_ERR_NULL, "%s: data is NULL", name);
   if (t->dtype != LCSA_DTYPE_BF16) return fail(LCSA_ERR_INVALID, "%s: dtype must be bf16", name);
@@ -67,9 +69,17 @@ lcsa_status check_view(const char* name, const lcsa_tensor* t, int64_t tokens, i
     return fail(LCSA_ERR_INVALID, "%s: strides must be positive (batch stride >= 0)", name);
   if (t->stride_b % 8 || t->stride_s % 8 || t->stride_h % 8)
     return fail(LCSA_ERR_ALIGN, "%s: strides must be multiples of 8 elements", name);
-  (void)tokens;
-  (void)heads;
+  if (t->batch != batch || t->tokens != tokens || t->heads != heads || t->head_dim != kHeadDim)
+    return fail(LCSA_ERR_SHAPE, "%s: extents [%lld, %lld, %lld, %lld], the plan needs [%d, %lld, %d, %d]",
+                name, (long long)t->batch, (long long)t->tokens, (long long)t->heads,
+                (long long)t->head_dim, batch, (long long)tokens, heads, kHeadDim);
   return LCSA_OK;
+}
+
+// Tokens of a K/V view: the contiguous window, or every slot of a ring.
+int64_t kv_view_tokens(const lcsa_plan_s* p, const lcsa_kv_ring* ring) {
+  return ring ? static_cast<int64_t>(ring->slots) * p->desc.grid_h * p->desc.grid_w
+              : p->info.kv_tokens;
 }
 
 // Magic multiplier for n / d with 0 <= n < 2^31 and d >= 1 (round-up
@@ -135,8 +145,8 @@ View make_view(const lcsa_tensor* t) {
 // (the newest new_frames frames are pooled into the caller's cache).
 // Rotary tables and the rotated Q / K outputs of lcsa_select_rope and
 // lcsa_select_ring_rope.
-lcsa_status check_rope(const char* fn, const lcsa_rope* rope, const lcsa_tensor* q_rot,
-                       const lcsa_tensor* k_rot) {
+lcsa_status check_rope(const char* fn, const lcsa_plan_s* plan, const lcsa_kv_ring* ring,
+                       const lcsa_rope* rope, const lcsa_tensor* q_rot, const lcsa_tensor* k_rot) {
   if (!rope) return fail(LCSA_ERR_NULL, "%s: rope is NULL", fn);
   const int pt = rope->pairs_t, ph = rope->pairs_h, pw = rope->pairs_w;
   if (pt < 0 || ph < 0 || pw < 0 || pt + ph + pw != kHeadDim / 2 || rope->reserved != 0)
@@ -149,8 +159,9 @@ lcsa_status check_rope(const char* fn, const lcsa_rope* rope, const lcsa_tensor*
     if (reinterpret_cast<uintptr_t>(tb) % 8)
       return fail(LCSA_ERR_ALIGN, "%s: rotary tables must be 8-byte aligned", fn);
   lcsa_status st;
-  if ((st = check_view("q_rot", q_rot, 0, 0))) return st;
-  if ((st = check_view("k_rot", k_rot, 0, 0))) return st;
+  const int batch = plan->desc.batch, heads = plan->desc.heads;
+  if ((st = check_view("q_rot", q_rot, batch, plan->info.q_tokens, heads))) return st;
+  if ((st = check_view("k_rot", k_rot, batch, kv_view_tokens(plan, ring), heads))) return st;
   return LCSA_OK;
 }
 
@@ -164,9 +175,11 @@ lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
-  if ((st = check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
-  if ((st = check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
-  if (rope && (st = check_rope(fn, rope, q_rot, k_rot))) return st;
+  const int batch = plan->desc.batch, heads = plan->desc.heads;
+  if (ring && (st = check_ring(fn, plan, ring))) return st;
+  if ((st = check_view("q", q, batch, in.q_tokens, heads))) return st;
+  if ((st = check_view("k", k, batch, kv_view_tokens(plan, ring), heads))) return st;
+  if (rope && (st = check_rope(fn, plan, ring, rope, q_rot, k_rot))) return st;
   if (!d_row_ptr || !d_col_idx) return fail(LCSA_ERR_NULL, "%s: CSR buffers are NULL", fn);
   if (d_tau && in.rows * static_cast<int64_t>(in.max_window) >= INT32_MAX)
     return fail(LCSA_ERR_SHAPE, "%s: %lld rows of %d entries exceed int32 CSR", fn,
@@ -234,10 +247,13 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
-  if ((st = check_view("q", q, in.q_tokens, plan->desc.heads))) return st;
-  if ((st = check_view("k", k, in.kv_tokens, plan->desc.heads))) return st;
-  if ((st = check_view("v", v, in.kv_tokens, plan->desc.heads))) return st;
-  if ((st = check_view("o", o, in.q_tokens, plan->desc.heads))) return st;
+  const int batch = plan->desc.batch, heads = plan->desc.heads;
+  if (ring && (st = check_ring(fn, plan, ring))) return st;
+  const int64_t kv_tokens = kv_view_tokens(plan, ring);
+  if ((st = check_view("q", q, batch, in.q_tokens, heads))) return st;
+  if ((st = check_view("k", k, batch, kv_tokens, heads))) return st;
+  if ((st = check_view("v", v, batch, kv_tokens, heads))) return st;
+  if ((st = check_view("o", o, batch, in.q_tokens, heads))) return st;
   if (!d_row_ptr) return fail(LCSA_ERR_NULL, "%s: row_ptr is NULL", fn);
   if (nnz < 0) return fail(LCSA_ERR_INVALID, "%s: nnz %lld < 0", fn, (long long)nnz);
   if (nnz > 0 && !d_col_idx) return fail(LCSA_ERR_NULL, "%s: col_idx is NULL", fn);

@@ -43,13 +43,14 @@
 extern "C" {
 #endif
 
-#define LCSA_ABI_VERSION 5
+#define LCSA_ABI_VERSION 6
 
 typedef int32_t lcsa_status;
 #define LCSA_OK 0
 #define LCSA_ERR_NULL 1       /* a required pointer is NULL */
 #define LCSA_ERR_INVALID 2    /* a descriptor value is out of range */
-#define LCSA_ERR_SHAPE 3      /* grid not tileable / sizes beyond limits */
+#define LCSA_ERR_SHAPE 3      /* grid not tileable / sizes beyond limits /
+                                 tensor extents differ from the plan's */
 #define LCSA_ERR_ALIGN 4      /* data or strides not 16-byte aligned */
 #define LCSA_ERR_WORKSPACE 5  /* workspace missing or too small */
 #define LCSA_ERR_DEVICE 6     /* no current HIP device, or it is not gfx950 */
@@ -101,7 +102,13 @@ typedef struct lcsa_desc {
 /* A device tensor view of logical shape [batch, tokens, heads, head_dim].
  * data must be 16-byte aligned and stride_b/stride_s/stride_h (in elements)
  * multiples of 8, so that every (token, head) row is a 256-byte aligned-16
- * contiguous vector.  dtype must be LCSA_DTYPE_BF16. */
+ * contiguous vector.  dtype must be LCSA_DTYPE_BF16.  The extents state the
+ * view's logical shape; every call checks them against the plan (the plan's
+ * batch and heads, head_dim 128, and the call's token count: q_tokens for
+ * queries and outputs, kv_tokens for a contiguous K/V window, slots *
+ * grid_h * grid_w for a frame ring) and returns LCSA_ERR_SHAPE on a
+ * mismatch.  The library cannot see the allocation behind data: the caller
+ * guarantees that every element the extents and strides address exists. */
 typedef struct lcsa_tensor {
   void* data;
   int32_t dtype;
@@ -109,6 +116,10 @@ typedef struct lcsa_tensor {
   int64_t stride_b;
   int64_t stride_s;
   int64_t stride_h;
+  int64_t batch;
+  int64_t tokens;
+  int64_t heads;
+  int64_t head_dim;
 } lcsa_tensor;
 
 /* Everything the plan derived from a descriptor. */
@@ -141,9 +152,14 @@ typedef struct lcsa_plan_info {
 typedef struct lcsa_plan_s* lcsa_plan_t;
 
 /* Validate a descriptor and precompute geometry, budget, window sizes and the
- * CSR row pointer.  Host only: needs no GPU.  On success *out owns a new plan
- * (release with lcsa_plan_destroy); it is immutable and may be shared across
- * threads and streams.  Errors: NULL, INVALID, SHAPE, INTERNAL. */
+ * CSR row pointer.  The controls are those of the streaming pipeline: the
+ * kept-block budget from topk_ratio, the spatial window local_range and the
+ * KV window length from kv_ratio (FlashVSR Inference skill page,
+ * "Non-Negotiable Streaming Contract"), over chunks of latent frames (a
+ * 6-frame first chunk and 2-frame stream chunks on the NxDI FlashVSR contrib
+ * page, "Description").  Host only: needs no GPU.  On success *out owns a new
+ * plan (release with lcsa_plan_destroy); it is immutable and may be shared
+ * across threads and streams.  Errors: NULL, INVALID, SHAPE, INTERNAL. */
 lcsa_status lcsa_plan_create(const lcsa_desc* desc, lcsa_plan_t* out);
 
 /* Release a plan; NULL is a no-op. */
@@ -167,7 +183,11 @@ lcsa_status lcsa_plan_window(lcsa_plan_t plan, int32_t qb, int32_t* host_out,
  * (float64 sums of the bf16 values), score each query block against every
  * key block of its window (float64 dot products), keep the k best
  * (descending score, ties to the lower block index) and emit them ascending
- * as the CSR block mask.
+ * as the CSR block mask.  Pooling and mask selection are the attention glue
+ * and the mask is built as CSR on the FlashVSR Hopper PR page ("What Was
+ * Actually Slow"; "Rebuild sparse attention for Hopper"); candidates are the
+ * key blocks of a spatial window around the query block (agentlens FlashVSR
+ * summary, "How it works", item 2).
  *  q, k            device views (shape [batch, q_tokens | kv_tokens, heads,
  *                  128]), read only.
  *  d_row_ptr       device int32[rows + 1], written (equal to the plan's).

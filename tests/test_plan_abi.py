@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lcsa.abi_version() == 5
+    assert lcsa.abi_version() == 6
     lib = ctypes.CDLL(lcsa.lib_path())
     lib.lcsa_status_string.restype = ctypes.c_char_p
     texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
@@ -132,8 +132,17 @@ def test_row_ptr_capacity_and_window_range():
     assert ei.value.name == "LCSA_ERR_INVALID"
 
 
-def _fake_view(addr=0x10000, sb=0, ss=256, sh=128):
-    return lcsa.LcsaTensor(data=addr, dtype=1, reserved=0, stride_b=sb, stride_s=ss, stride_h=sh)
+def _fake_view(addr=0x10000, sb=0, ss=256, sh=128, plan=None, tokens="q", heads=None, dim=128):
+    """A view of a fake device address with the extents a plan expects:
+    tokens "q" (q_tokens), "kv" (kv_tokens) or a number."""
+    p = plan if plan is not None else _TINY
+    t = {"q": p.info["q_tokens"], "kv": p.info["kv_tokens"]}.get(tokens, tokens)
+    return lcsa.LcsaTensor(data=addr, dtype=1, reserved=0, stride_b=sb, stride_s=ss, stride_h=sh,
+                           batch=p.desc["batch"], tokens=t,
+                           heads=p.desc["heads"] if heads is None else heads, head_dim=dim)
+
+
+_TINY = lcsa.Plan.from_desc(li.CONFIGS["tiny"])
 
 
 def _select(p, q, k, rp=0x20000, ci=0x30000, ws=0x40000, ws_bytes=None):
@@ -151,7 +160,7 @@ def _attend(p, q, k, v, o, nnz=8, ws=None, ws_bytes=0):
 def test_entry_point_validation_statuses():
     """Argument checks run on the host before any HIP call; the fake device
     addresses are never dereferenced because every call here fails first."""
-    p = lcsa.Plan.from_desc(li.CONFIGS["tiny"])
+    p = _TINY
     good = _fake_view()
     assert _select(p, _fake_view(addr=0x10008), good) == 4            # ALIGN data
     assert _select(p, _fake_view(ss=250), good) == 4                  # ALIGN stride
@@ -167,26 +176,49 @@ def test_entry_point_validation_statuses():
     assert lcsa._lib.lcsa_select(None, None, None, None, None, None, None, 0, None) == 1
     big = lcsa.Plan.from_desc(dict(li.CONFIGS["first_2048x3840"], local_range=15))
     assert big.info["max_window"] > 1024
-    assert _select(big, good, good) == 3                              # SHAPE: window limit
+    bq, bk = _fake_view(plan=big), _fake_view(plan=big, tokens="kv")
+    assert _select(big, bq, bk) == 3                                  # SHAPE: window limit
+
+
+def test_entry_point_extent_statuses():
+    """Tensor extents that disagree with the plan are LCSA_ERR_SHAPE, checked
+    on the host before any HIP call (after pointer, dtype and alignment)."""
+    p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])    # q 4096 tokens, kv 6144
+    q, kv = _fake_view(plan=p), _fake_view(plan=p, tokens="kv")
+    assert p.info["q_tokens"] != p.info["kv_tokens"]
+    assert _select(p, kv, kv) == 3                                    # q with kv's tokens
+    assert _select(p, q, q) == 3                                      # k with q's tokens
+    assert _select(p, q, _fake_view(plan=p, tokens="kv", heads=2)) == 3
+    assert _select(p, q, _fake_view(plan=p, tokens="kv", dim=64)) == 3
+    wrong_batch = _fake_view(plan=p); wrong_batch.batch = 2
+    assert _select(p, wrong_batch, kv) == 3
+    assert _attend(p, q, kv, kv, kv) == 3                             # o with kv's tokens
+    assert _attend(p, q, kv, q, q) == 3                               # v with q's tokens
+    assert _attend(p, q, _fake_view(plan=p, tokens=0), kv, q) == 3
+    assert _select(p, _fake_view(plan=p, addr=0x10008, tokens=1), kv) == 4   # ALIGN first
+    if not torch.cuda.is_available():
+        assert _select(p, q, kv) == 6 and _attend(p, q, kv, kv, q) == 6      # DEVICE
 
 
 def test_ring_entry_point_validation_statuses():
     """Frame-ring arguments are checked on the host before any HIP call."""
     p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])      # kv_frames 3
     kvf = p.info["kv_frames"]
-    good = _fake_view()
+    q = _fake_view(plan=p)
+    ft = p.desc["grid_h"] * p.desc["grid_w"]
+    ring4 = _fake_view(plan=p, tokens=4 * ft)                # a ring of 4 frame slots
     lib = lcsa._lib
     ws, wsb = 0x40000, p.info["select_workspace_bytes"]
 
-    def sel(ring, new=1, kc=0x80000):
+    def sel(ring, new=1, kc=0x80000, kview=ring4):
         r = ctypes.byref(ring) if ring is not None else None
-        return lib.lcsa_select_ring(p.handle, ctypes.byref(good), ctypes.byref(good), r, new, kc,
+        return lib.lcsa_select_ring(p.handle, ctypes.byref(q), ctypes.byref(kview), r, new, kc,
                                     0x20000, 0x30000, None, ws, wsb, None)
 
-    def att(ring):
+    def att(ring, kview=ring4):
         r = ctypes.byref(ring) if ring is not None else None
-        return lib.lcsa_attend_ring(p.handle, ctypes.byref(good), ctypes.byref(good),
-                                    ctypes.byref(good), r, 0x20000, 0x30000, 8, ctypes.byref(good),
+        return lib.lcsa_attend_ring(p.handle, ctypes.byref(q), ctypes.byref(kview),
+                                    ctypes.byref(kview), r, 0x20000, 0x30000, 8, ctypes.byref(q),
                                     None, None, 0, None)
     ok = lcsa.kv_ring(4, [3, 0, 1])
     assert sel(None) == 1                                            # NULL ring
@@ -197,6 +229,8 @@ def test_ring_entry_point_validation_statuses():
     assert sel(ok, kc=0) == 1                                        # NULL cache
     assert sel(ok, kc=0x80008) == 4                                  # ALIGN cache
     assert att(None) == 1 and att(lcsa.kv_ring(2, [0, 1, 2])) == 2
+    kv3 = _fake_view(plan=p, tokens="kv")                     # 3 frames: not the ring's 4
+    assert sel(ok, kview=kv3) == 3 and att(ok, kview=kv3) == 3      # SHAPE: ring extents
     if not torch.cuda.is_available():
         assert sel(ok) == 6 and att(ok) == 6                         # DEVICE on CPU hosts
     too_many = dict(li.CONFIGS["tiny"], q_frames=65, kv_ratio=0.0)
@@ -208,7 +242,8 @@ def test_ring_entry_point_validation_statuses():
 def test_rope_entry_point_validation_statuses():
     """Rotary-embedding arguments are checked on the host before any HIP call."""
     p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])
-    good = _fake_view()
+    q, kv = _fake_view(plan=p), _fake_view(plan=p, tokens="kv")
+    ring4 = _fake_view(plan=p, tokens=4 * p.desc["grid_h"] * p.desc["grid_w"])
     lib = lcsa._lib
     ws, wsb = 0x40000, p.info["select_workspace_bytes"]
 
@@ -216,18 +251,18 @@ def test_rope_entry_point_validation_statuses():
         return lcsa.LcsaRope(pairs_t=pt, pairs_h=ph, pairs_w=pw, reserved=reserved,
                              table_t=tt, table_h=th, table_w=tw)
 
-    def sel(r, q_rot=good, k_rot=good):
+    def sel(r, q_rot=q, k_rot=kv):
         rr = ctypes.byref(r) if r is not None else None
         qr = ctypes.byref(q_rot) if q_rot is not None else None
         kr = ctypes.byref(k_rot) if k_rot is not None else None
-        return lib.lcsa_select_rope(p.handle, ctypes.byref(good), ctypes.byref(good), rr, qr, kr,
+        return lib.lcsa_select_rope(p.handle, ctypes.byref(q), ctypes.byref(kv), rr, qr, kr,
                                     0x20000, 0x30000, None, ws, wsb, None)
 
-    def sel_ring(r, ring, new=1):
+    def sel_ring(r, ring, new=1, k_rot=ring4):
         rr = ctypes.byref(r) if r is not None else None
-        return lib.lcsa_select_ring_rope(p.handle, ctypes.byref(good), ctypes.byref(good),
-                                         ctypes.byref(ring), new, 0x80000, rr, ctypes.byref(good),
-                                         ctypes.byref(good), 0x20000, 0x30000, None, ws, wsb, None)
+        return lib.lcsa_select_ring_rope(p.handle, ctypes.byref(q), ctypes.byref(ring4),
+                                         ctypes.byref(ring), new, 0x80000, rr, ctypes.byref(q),
+                                         ctypes.byref(k_rot), 0x20000, 0x30000, None, ws, wsb, None)
     assert sel(None) == 1                                             # NULL rope
     assert sel(rope(pt=23)) == 2 and sel(rope(pt=-1, ph=44)) == 2     # pairs must sum to 64
     assert sel(rope(reserved=1)) == 2
@@ -235,7 +270,9 @@ def test_rope_entry_point_validation_statuses():
     assert sel(rope(pt=0, ph=43, tt=0)) != 1                          # no pairs: table may be NULL
     assert sel(rope(tw=0x70004)) == 4                                 # ALIGN table
     assert sel(rope(), q_rot=None) == 1                               # NULL output
-    assert sel(rope(), k_rot=_fake_view(addr=0x10008)) == 4           # ALIGN output
+    assert sel(rope(), k_rot=_fake_view(plan=p, addr=0x10008, tokens="kv")) == 4  # ALIGN output
+    assert sel(rope(), q_rot=kv) == 3 and sel(rope(), k_rot=q) == 3   # SHAPE: output extents
+    assert sel_ring(rope(), lcsa.kv_ring(4, [3, 0, 1]), k_rot=kv) == 3
     assert sel_ring(None, lcsa.kv_ring(4, [3, 0, 1])) == 1
     assert sel_ring(rope(), lcsa.kv_ring(4, [3, 4, 1])) == 2          # slot out of range
     assert sel_ring(rope(), lcsa.kv_ring(4, [3, 0, 1]), new=9) == 2
@@ -246,7 +283,7 @@ def test_rope_entry_point_validation_statuses():
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device status on CPU hosts")
 def test_no_device_status_on_cpu_host():
-    p = lcsa.Plan.from_desc(li.CONFIGS["tiny"])
+    p = _TINY
     good = _fake_view()
     assert _select(p, good, good) == 6                                # DEVICE
     assert _attend(p, good, good, good, good) == 6
@@ -269,7 +306,8 @@ def test_threshold_entry_point_validation_statuses():
     """Arguments of the steady-threshold calls are checked on the host before
     any HIP call; the ring and the rotary tables are each optional."""
     p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])
-    good = _fake_view()
+    q, kv = _fake_view(plan=p), _fake_view(plan=p, tokens="kv")
+    ring4 = _fake_view(plan=p, tokens=4 * p.desc["grid_h"] * p.desc["grid_w"])
     lib = lcsa._lib
     ws, wsb = 0x40000, p.info["select_workspace_bytes"]
     ok_ring = lcsa.kv_ring(4, [3, 0, 1])
@@ -277,13 +315,15 @@ def test_threshold_entry_point_validation_statuses():
     def steady(kth=0x90000, ring=None, new=1, kc=0x80000, rope=None):
         rg = ctypes.byref(ring) if ring is not None else None
         rp = ctypes.byref(rope) if rope is not None else None
-        return lib.lcsa_select_steady(p.handle, ctypes.byref(good), ctypes.byref(good), rg, new,
-                                      kc, rp, ctypes.byref(good), ctypes.byref(good), 0x20000,
+        k = ring4 if ring is not None else kv
+        return lib.lcsa_select_steady(p.handle, ctypes.byref(q), ctypes.byref(k), rg, new,
+                                      kc, rp, ctypes.byref(q), ctypes.byref(k), 0x20000,
                                       0x30000, kth, None, ws, wsb, None)
 
     def reuse(tau=0x90000, ring=None, new=1, kc=0x80000):
         rg = ctypes.byref(ring) if ring is not None else None
-        return lib.lcsa_select_reuse(p.handle, ctypes.byref(good), ctypes.byref(good), rg, new, kc,
+        k = ring4 if ring is not None else kv
+        return lib.lcsa_select_reuse(p.handle, ctypes.byref(q), ctypes.byref(k), rg, new, kc,
                                      None, None, None, tau, 0x20000, 0x30000, None, ws, wsb, None)
     assert steady(kth=0) == 1 and reuse(tau=0) == 1                  # NULL thresholds
     assert steady(kth=0x90004) == 4 and reuse(tau=0x90004) == 4      # ALIGN thresholds
