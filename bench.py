@@ -12,14 +12,17 @@ Prints ONE JSON line.  value = useful attention TFLOP/s of the whole step
 not count), ms_per_step = select+attend ms per chunk.  roofline = the attend
 kernel (MFMA-bound) timed with HIP events on its stream; select_roofline =
 the select entry point (pool + select kernels) against HBM bandwidth;
-cpu_baseline = the float64 CPU oracle on a bounded sample of the same
-workload.  Means, medians and p10/p90 come from the warm steps; cold_cache
+cpu_baseline = the float64 CPU oracle on the same step, its heads spread
+over worker processes (1 warm-up and 3 timed runs, medians); parity = the
+GPU's CSR, O and LSE of that step against the oracle's, on every row and
+element; workloads = select and attend medians of the other named workloads
+in the same run.  Means, medians and p10/p90 come from the warm steps; cold_cache
 repeats --cold-steps steps after a 512 MiB fill that evicts L2 and the
 memory-side cache before each one; graph times --graph-steps replays of
 select + attend captured once in a HIP graph.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--cold-steps N] [--graph-steps N]
+                  [--no-workloads] [--cold-steps N] [--graph-steps N]
   python bench.py --workload stream_768x1280 --ring   # streaming steady state
   python bench.py --rope                               # rotary embedding fused into select
   python bench.py --workload stream_768x1280 --reuse [--ring]   # steady threshold reuse
@@ -60,51 +63,115 @@ def _traffic(workload):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(name, desc, inp, useful_flops, rope_tables=None):
-    """Time the oracle as it stands on a bounded sample and scale to a step
-    (with rope_tables, the oracle's rotary embedding of Q and K first)."""
+NEAR_TIE_REL, NEAR_TIE_FLOOR = 1e-4, 1e-6     # k-th score gap that counts as a near-tie
+MAX_ABS_ERR, MIN_COSINE = 1e-2, 0.9999          # attention parity bar
+
+
+def _mask_parity(g, window, rp_ref, ci_ref, s_ref, rp_gpu, ci_gpu):
+    """Rows whose GPU blocks differ from the oracle's, and how many of them
+    are near-ties (k-th and (k+1)-th oracle window scores within 1e-4
+    relative, or 1e-6 of the row's largest |score|, with every GPU-kept
+    block scored inside that band)."""
     import numpy as np
-    import lcsa_inputs as li
+    mism, ties = [], 0
+    if not np.array_equal(np.asarray(rp_gpu, np.int64), rp_ref):
+        return list(range(len(rp_ref) - 1)), 0
+    for r in range(len(rp_ref) - 1):
+        a = ci_gpu[rp_ref[r]:rp_ref[r + 1]]
+        b = ci_ref[rp_ref[r]:rp_ref[r + 1]]
+        if np.array_equal(a, b):
+            continue
+        mism.append(r)
+        bb, rem = divmod(r, g.heads * g.nqb)
+        h, qb = divmod(rem, g.nqb)
+        e = window(g, qb)
+        srt = np.sort(s_ref[bb, h, qb, e])[::-1]
+        kk = len(b)
+        if kk >= len(e):
+            continue
+        sk, sk1 = srt[kk - 1], srt[kk]
+        band = max(NEAR_TIE_REL * max(abs(sk), abs(sk1)), NEAR_TIE_FLOOR * np.abs(srt).max())
+        if sk - sk1 <= band and s_ref[bb, h, qb, a].min() >= sk1 - band:
+            ties += 1
+    return mism, ties
+
+
+def cpu_baseline(name, desc, inp, useful_flops, gpu, runs=3):
+    """The oracle as it stands, timed on the host cores on the whole step of
+    the workload: select and attention, each head on one of a pool of
+    worker processes (one BLAS thread each); 1 warm-up run and `runs` timed
+    runs, medians.  The warm-up run's results are also the reference of the
+    parity record: the GPU's CSR against the oracle's (mismatches, near-
+    ties) and the GPU's O and LSE against the oracle's attention over the
+    GPU's own mask, on every element."""
+    import numpy as np
     import oracle
+    from oracle.parallel import OraclePool
+    g = oracle.geometry(desc)
+    rp_g, ci_g, o_g, lse_g = gpu
+    with OraclePool(desc, inp.q, inp.k, inp.v) as pool:
+        rp, ci, s, _ = pool.select()                       # warm-up, and the reference
+        o_ref, lse_ref, _ = pool.attend(rp, ci)
+        t_sel, t_att = [], []
+        for _ in range(runs):
+            t_sel.append(pool.select()[3])
+            t_att.append(pool.attend(rp, ci)[2])
+        mism, ties = _mask_parity(g, oracle.window, rp, ci, s, rp_g, ci_g)
+        if mism:  # attention is compared on the GPU's own mask
+            for b, h, qtok, orow, lrow in pool.attend_rows(rp_g, ci_g, mism):
+                o_ref[b, qtok, h] = orow
+                lse_ref[b, h, qtok] = lrow
+        workers = pool.workers
+    a, bref = o_g.astype(np.float64).ravel(), o_ref.ravel()
+    cos = float(a @ bref / (np.linalg.norm(a) * np.linalg.norm(bref)))
+    head_cos = []
+    for b in range(g.batch):
+        for h in range(g.heads):
+            x, y = o_g[b, :, h].astype(np.float64).ravel(), o_ref[b, :, h].ravel()
+            head_cos.append(float(x @ y / (np.linalg.norm(x) * np.linalg.norm(y))))
+    fin = np.isfinite(lse_ref)
+    parity = {
+        "reference": "float64 oracle: its own top-k CSR; attention over the GPU's CSR",
+        "rows": int(len(rp) - 1),
+        "mask_rows_differing": len(mism),
+        "mask_near_ties": int(ties),
+        "mask_mismatches_not_near_tie": len(mism) - int(ties),
+        "attend_elements": int(o_g.size),
+        "attend_max_abs_err": float(np.abs(o_g.astype(np.float64) - o_ref).max()),
+        "attend_cosine": cos,
+        "attend_worst_head_cosine": min(head_cos),
+        "lse_max_abs_err": float(np.abs(lse_g[fin] - lse_ref[fin]).max()),
+        "bar": {"max_abs_err": MAX_ABS_ERR, "cosine": MIN_COSINE},
+    }
+    parity["pass"] = bool(parity["mask_mismatches_not_near_tie"] == 0
+                          and parity["attend_max_abs_err"] <= MAX_ABS_ERR
+                          and cos >= MIN_COSINE)
+    sel_s, att_s = float(np.median(t_sel)), float(np.median(t_att))
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        blas_threads = 1
-    g = oracle.geometry(desc)
-    qf, kf, vf = (li.bf16_bits_to_f32(x) for x in (inp.q, inp.k, inp.v))
-    t0 = time.perf_counter()
-    if rope_tables is not None:
-        tab = oracle.RopeTables(t=rope_tables["t"], h=rope_tables["h"], w=rope_tables["w"])
-        qf, kf = oracle.rope_q(g, qf, tab), oracle.rope_k(g, kf, tab)
-    rp, ci, _ = oracle.select(g, qf, kf)
-    t_sel = time.perf_counter() - t0
-    rows = len(rp) - 1
-    # rows sampled evenly; grow the sample until ~10 s of attention work
-    n = max(8, rows // 64)
-    t_att, done = 0.0, 0
-    while True:
-        sample = np.linspace(0, rows - 1, n).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.attend_rows(g, qf, kf, vf, rp, ci, sample)
-        t_att = time.perf_counter() - t0
-        done = n
-        if t_att >= 8.0 or n >= rows:
-            break
-        n = min(rows, int(n * max(2.0, 10.0 / max(t_att, 1e-3))))
-    step_s = t_sel + t_att * rows / done
-    return {
-        "value": useful_flops / step_s / 1e12,
+        blas = None
+    base = {
+        "value": useful_flops / (sel_s + att_s) / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": int(workers),
         "kind": "oracle",
-        "ms_per_step": step_s * 1e3,
-        "sample": (f"{name}: oracle {'rotary embedding + ' if rope_tables is not None else ''}"
-                   f"select on all {rows} CSR rows ({t_sel:.2f} s) + oracle "
-                   f"attention on {done} of {rows} rows ({t_att:.2f} s), scaled to the full "
-                   f"step; float64 numpy, {blas_threads} BLAS threads, "
-                   f"{len(os.sched_getaffinity(0))} host cores visible"),
+        "ms_per_step": (sel_s + att_s) * 1e3,
+        "select_s_median": sel_s,
+        "attend_s_median": att_s,
+        "select_s_runs": t_sel,
+        "attend_s_runs": t_att,
+        "processes": int(workers),
+        "blas_threads_per_process": 1,
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+        "parent_blas_threads": blas,
+        "sample": (f"{name}: the whole step, oracle select and attention on all "
+                   f"{len(rp) - 1} CSR rows, one (batch, head) per task on {workers} worker "
+                   f"processes x 1 BLAS thread; 1 warm-up + {runs} timed runs, medians; "
+                   f"float64 numpy"),
     }
+    return base, parity
 
 
 def copy_calibration():
@@ -127,7 +194,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="first_768x1280")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle's CPU timing and the parity record built from it")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only the chosen workload, not the other named ones")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed after a 512 MiB cache flush each (0: none)")
@@ -478,9 +548,85 @@ def main():
         },
         "device": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline and not args.reuse:
-        res["cpu_baseline"] = cpu_baseline(name, desc, inp, flops, tabs if args.rope else None)
+    plain = not (args.reuse or args.rope or args.ring)
+    if not args.no_cpu_baseline and plain:
+        # the GPU's CSR, O and LSE of one more step, for the parity record
+        pplan = lcsa.Plan.from_desc(desc)
+        rp_g, ci_g = lcsa.select(pplan, q, k, workspace=ws)
+        o_g, lse_g = lcsa.attend(pplan, q, k, v, rp_g, ci_g, return_lse=True, workspace=att_ws)
+        torch.cuda.synchronize()
+        gpu = (rp_g.cpu().numpy().astype(np.int64), ci_g.cpu().numpy().astype(np.int64),
+               o_g.float().cpu().numpy(), lse_g.cpu().numpy())
+        res["cpu_baseline"], res["parity"] = cpu_baseline(name, desc, inp, flops, gpu)
+    if not args.no_workloads and plain:
+        del q, k, v, out, att_ws, ws
+        torch.cuda.empty_cache()
+        res["workloads"] = time_workloads([n for n in li.PAGE_WORKLOADS if n != name],
+                                          args.seed, dev, stream)
     print(json.dumps(res), flush=True)
+
+
+def time_workloads(names, seed, dev, stream):
+    """Select and attend medians of the other named workloads, timed with
+    HIP events on the launch stream in this same run (10 warm-up steps, then
+    20 timed; 10 at the 184320-token chunk)."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_lcsa_amd as lcsa
+    import lcsa_inputs as li
+
+    out = {}
+    for name in names:
+        desc = dict(li.CONFIGS[name])
+        inp = li.generate(desc, seed=seed)
+
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = up(inp.q), up(inp.k), up(inp.v)
+        plan = lcsa.Plan.from_desc(desc)
+        info = plan.info
+        ws = torch.empty(max(int(info["select_workspace_bytes"]), 256), dtype=torch.uint8, device=dev)
+        att_ws = torch.empty(int(info["attend_workspace_bytes"]), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        n = 10 if info["q_tokens"] > 100000 else 20
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            rp, ci = lcsa.select(plan, q, k, workspace=ws)
+            if ev:
+                ev[1].record(stream)
+            lcsa.attend(plan, q, k, v, rp, ci, out=o, workspace=att_ws)
+            if ev:
+                ev[2].record(stream)
+        for _ in range(10):
+            step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        sel = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+        att = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+        both = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+        flops = float(info["useful_flops"])
+        sel_bytes = (2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + info["kv_tokens"])
+                     + 4 * (info["rows"] + 1 + info["nnz"]))
+        out[name] = {
+            "steps": n, "q_tokens": info["q_tokens"], "kv_tokens": info["kv_tokens"],
+            "block": [info["block_h"], info["block_w"]], "k": info["k"],
+            "selected_pairs": info["nnz"], "useful_tflop": flops / 1e12,
+            "inputs_sha256": inp.sha256,
+            "select_ms_median": sel, "attend_ms_median": att, "select_attend_ms_median": both,
+            "attend_tflops": flops / (att * 1e-3) / 1e12,
+            "attend_frac_of_bf16_peak": flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "select_gbs": sel_bytes / (sel * 1e-3) / 1e9,
+            "select_frac_of_hbm": sel_bytes / (sel * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "step_tflops": flops / (both * 1e-3) / 1e12,
+        }
+        print(f"bench: {name} select {sel:.4f} ms, attend {att:.4f} ms", file=sys.stderr, flush=True)
+        del q, k, v, o, ws, att_ws, inp
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -41,3 +41,36 @@ def test_committed_traffic_record_is_well_formed():
     assert len(entry["attend_src_sha256"]) == 64
     # at least the algorithmic Q + K + V + O bytes of one launch (4 x 70.8 MB)
     assert entry["bytes_per_launch"] >= 4 * 23040 * 12 * 128 * 2
+
+
+def test_parity_record_from_the_cpu_baseline_leg():
+    """The bench's parity record, fed the oracle's own results as the GPU
+    side (O rounded to bf16), passes with no mask mismatch; a row with one
+    block swapped for a low-scoring one counts as a mismatch that is not a
+    near-tie, and fails the record."""
+    import numpy as np
+    import lcsa_inputs as li
+    import oracle
+    name = "small_edges"
+    desc = li.CONFIGS[name]
+    inp = li.generate(desc, seed=3)
+    g = oracle.geometry(desc)
+    q, k, v = (li.bf16_bits_to_f64(x) for x in (inp.q, inp.k, inp.v))
+    rp, ci, s = oracle.select(g, q, k)
+    o, lse = oracle.attend(g, q, k, v, rp, ci)
+    o_bf16 = li.bf16_bits_to_f32(li.f32_to_bf16_bits(o.astype(np.float32)))
+    base, par = bench.cpu_baseline(name, desc, inp, oracle.useful_flops(g, rp),
+                                   (rp, ci, o_bf16, lse.astype(np.float32)), runs=1)
+    assert par["pass"] and par["mask_rows_differing"] == 0
+    assert par["attend_elements"] == o.size and par["attend_cosine"] > 0.9999
+    assert base["kind"] == "oracle" and base["cores"] >= 1 and len(base["attend_s_runs"]) == 1
+    # swap row 0's lowest kept block for the window block with the lowest score
+    ci2 = ci.copy()
+    e = oracle.window(g, 0)
+    worst = int(e[np.argmin(s[0, 0, 0, e])])
+    row = ci2[rp[0]:rp[1]]
+    assert worst not in row
+    row[np.argmin(s[0, 0, 0, row])] = worst
+    ci2[rp[0]:rp[1]] = np.sort(row)
+    mism, ties = bench._mask_parity(g, oracle.window, rp, ci, s, rp, ci2)
+    assert mism == [0] and ties == 0

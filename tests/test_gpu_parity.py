@@ -5,9 +5,12 @@ Select: row_ptr bit-exact; pooled scores within 1e-12 of the row scale
 (both sides sum in float64); selected blocks identical except at near-ties
 (oracle k-th score gap <= 1e-4 relative), which are counted and reported.
 Attend: bf16 output within max |err| <= 1e-2 and cosine >= 0.9999 of the
-oracle run on the GPU's own mask; LSE within 2e-3.  Small grids are compared
-element by element in full; the page workloads at their full sizes are
-compared on sampled CSR rows that the oracle computes one by one."""
+oracle run on the GPU's own mask; LSE within 2e-3.  Small grids, the stream
+chunk and both 768-line first chunks are compared element by element on the
+whole tensor (the oracle spread over heads on worker processes); at the 4K
+chunk, every row the launch splits over several workgroups plus 768 rows
+(every head's corner and edge blocks, the rest at random) are compared."""
+import math
 import zlib
 
 import numpy as np
@@ -16,6 +19,7 @@ import torch
 
 import lcsa_inputs as li
 import oracle
+from oracle.parallel import OraclePool
 from gpu_util import (check_mask, compare_output, bf16_to_np, device_qkv, host_inputs,
                       oracle_select, say, to_device_bf16)
 
@@ -89,8 +93,98 @@ def _sample_rows(rows, n, seed):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_attend_parity_sampled(name):
+def split_tail_rows(plan):
+    """CSR rows that lcsa_attend (with its workspace) splits over several
+    workgroups on this GPU: the rows % slots last rows of the launch's
+    visiting order (square tiles of block positions, all query frames of a
+    tile together, head by head), when each gets at least two pieces."""
+    inf, d = plan.info, plan.desc
+    bt = inf["block_tokens"]
+    slots = torch.cuda.get_device_properties(0).multi_processor_count * (8 // (bt // 32))
+    rows = int(inf["rows"])
+    tail = rows % slots
+    if tail == 0 or min(slots // tail, min(inf["max_row_nnz"], 16)) < 2:
+        return []
+    nbh, nbw, nbf, nqb, qf = inf["nbh"], inf["nbw"], inf["blocks_per_frame"], inf["nqb"], d["q_frames"]
+    tile = int(math.sqrt((slots // 8) / qf) + 0.5)
+    tile = min(max(tile, 1), max(nbh, nbw))
+    out = []
+    for e in range(rows - tail, rows):
+        bh, r = divmod(e, nqb)
+        band = tile * nbw * qf
+        ty, r = divmod(r, band)
+        th = min(tile, nbh - ty * tile)
+        tx, r = divmod(r, th * tile * qf)
+        tw = min(tile, nbw - tx * tile)
+        tq, pp = divmod(r, th * tw)
+        py, px = divmod(pp, tw)
+        out.append(bh * nqb + tq * nbf + (ty * tile + py) * nbw + tx * tile + px)
+    return out
+
+
+@pytest.mark.parametrize("name", ["first_768x1280", "first_768x1408"])
+def test_attend_parity_whole_tensor(name):
+    """Every row of the 768-line first chunks against the oracle (run over
+    the GPU's own mask), including the rows of the split tail."""
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+    o1 = lcsa.attend(plan, q, k, v, rp, ci, split_tail=False)
+    torch.cuda.synchronize()
+    split = split_tail_rows(plan)
+    g = oracle.geometry(desc)
+    o_h, o1_h = bf16_to_np(o), bf16_to_np(o1)
+    differ = set()
+    for r in range(plan.info["rows"]):
+        bb, rem = divmod(r, g.heads * g.nqb)
+        h, qb = divmod(rem, g.nqb)
+        tok = oracle.block_tokens(g, qb)
+        if not np.array_equal(o_h[bb, tok, h], o1_h[bb, tok, h]):
+            differ.add(r)
+    say(f"  {name}: {len(split)} split-tail rows on this GPU, {len(differ)} rows differ from "
+        f"the unsplit launch")
+    assert differ <= set(split), "rows outside the computed split tail differ from unsplit"
+    _, inp = host_inputs(name)
+    with OraclePool(desc, inp.q, inp.k, inp.v) as pool:
+        o_ref, lse_ref, wall = pool.attend(rp.cpu().numpy().astype(np.int64),
+                                           ci.cpu().numpy().astype(np.int64))
+    say(f"  oracle attention on every row: {wall:.1f} s on {pool.workers} processes")
+    compare_output(o_h, o_ref, f"{name} whole tensor")
+    if split:
+        sel = np.zeros((g.batch, g.q_tokens, g.heads), dtype=bool)
+        for r in split:
+            bb, rem = divmod(r, g.heads * g.nqb)
+            h, qb = divmod(rem, g.nqb)
+            sel[bb, oracle.block_tokens(g, qb), h] = True
+        compare_output(o_h[sel], o_ref[sel], f"{name} split-tail rows")
+    lerr = float(np.abs(lse.cpu().numpy() - lse_ref).max())
+    say(f"  LSE max|err| {lerr:.3e}")
+    assert lerr <= LSE_TOL
+
+
+def _stratified_rows(g, n_random, seed):
+    """Every head's blocks at the frame's corners and edges (first and last
+    block row and column) of the first and last query frame, plus n_random
+    other rows."""
+    rows = set()
+    edge = [p for p in range(g.nbf)
+            if p // g.nbw in (0, g.nbh - 1) or p % g.nbw in (0, g.nbw - 1)]
+    rng = np.random.default_rng(seed)
+    for bh in range(g.batch * g.heads):
+        for tq in sorted({0, g.q_frames - 1}):
+            for p in rng.choice(edge, size=min(6, len(edge)), replace=False):
+                rows.add(bh * g.nqb + tq * g.nbf + int(p))
+    total = g.batch * g.heads * g.nqb
+    rest = [r for r in rng.choice(total, size=min(total, n_random + len(rows)), replace=False)
+            if r not in rows]
+    rows.update(int(r) for r in rest[:n_random])
+    rows.update([0, total - 1])
+    return sorted(rows)
+
+
+def test_attend_parity_sampled_4k():
+    name = "first_2048x3840"
     desc, q, k, v = device_qkv(name)
     plan = lcsa.Plan.from_desc(desc)
     rp, ci = lcsa.select(plan, q, k)
@@ -98,10 +192,14 @@ def test_attend_parity_sampled(name):
     torch.cuda.synchronize()
     _, inp = host_inputs(name)
     g = oracle.geometry(desc)
-    rows = _sample_rows(plan.info["rows"], 48, seed=zlib.crc32(name.encode()))
+    split = split_tail_rows(plan)
+    rows = sorted(set(_stratified_rows(g, 768, seed=zlib.crc32(name.encode()))) | set(split))
+    say(f"  {name}: {len(rows)} rows compared ({len(split)} split-tail rows on this GPU)")
+    assert len(rows) >= 768
     rp_h = rp.cpu().numpy().astype(np.int64)
     ci_h = ci.cpu().numpy().astype(np.int64)
-    ref = oracle.attend_rows(g, _f32(inp.q), _f32(inp.k), _f32(inp.v), rp_h, ci_h, rows)
+    with OraclePool(desc, inp.q, inp.k, inp.v) as pool:
+        ref = pool.attend_rows(rp_h, ci_h, rows)
     o_h = bf16_to_np(o)
     lse_h = lse.cpu().numpy()
     got, want, lerr = [], [], 0.0
