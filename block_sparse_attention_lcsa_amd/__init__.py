@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Plan", "LcsaError", "select", "attend", "select_ring", "attend_ring", "select_rope",
+__all__ = ["Plan", "LcsaError", "select", "select_noalloc", "attend", "select_ring", "attend_ring", "select_rope",
            "select_ring_rope", "rope", "select_steady", "select_reuse", "lib_path", "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,9 +47,10 @@ EXPORTS = [
     "lcsa_plan_create", "lcsa_plan_destroy", "lcsa_plan_get_info", "lcsa_plan_row_ptr",
     "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_select_rope",
     "lcsa_select_ring_rope", "lcsa_select_ring", "lcsa_attend_ring", "lcsa_select_steady",
-    "lcsa_select_reuse",
+    "lcsa_select_reuse", "lcsa_select_noalloc",
     "lcsa_status_string", "lcsa_last_error", "lcsa_abi_version",
 ]
+SELECT_NOALLOC_MAX_BYTES = 48 << 20
 MAX_KV_FRAMES = 64
 
 LCSA_DTYPE_BF16 = 1
@@ -118,6 +119,9 @@ _lib.lcsa_plan_window.restype = ctypes.c_int32
 _lib.lcsa_select.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
                              _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.lcsa_select.restype = ctypes.c_int32
+_lib.lcsa_select_noalloc.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                     _P, _P, _P, _P]
+_lib.lcsa_select_noalloc.restype = ctypes.c_int32
 _lib.lcsa_attend.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
                              ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_int64,
                              ctypes.POINTER(LcsaTensor), _P, _P, ctypes.c_size_t, _P]
@@ -288,6 +292,42 @@ def select(plan: Plan, q, k, return_scores: bool = False, workspace=None, stream
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream_ptr(q, stream))
     _check(st, "lcsa_select")
+    if return_scores:
+        return row_ptr, col_idx, scores
+    return row_ptr, col_idx
+
+
+def select_noalloc(plan: Plan, q, k, row_ptr=None, col_idx=None, return_scores: bool = False,
+                   stream=None):
+    """select without a workspace (lcsa_select_noalloc): the library's own
+    per-device scratch array holds the pooled vectors, so the C call
+    allocates nothing.  row_ptr / col_idx may be passed in (int32, rows + 1
+    and nnz entries) so that nothing is allocated here either.  Calls that
+    overlap on one device race on the scratch array."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    _check_shape(k, plan, "kv_tokens", "k")
+    inf = plan.info
+    dev = q.device
+    if row_ptr is None:
+        row_ptr = torch.empty(inf["rows"] + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(inf["nnz"], 1), dtype=torch.int32, device=dev)[: inf["nnz"]]
+    if row_ptr.dtype != torch.int32 or row_ptr.numel() != inf["rows"] + 1:
+        raise ValueError("row_ptr must be int32 [rows + 1]")
+    if col_idx.dtype != torch.int32 or col_idx.numel() != inf["nnz"]:
+        raise ValueError("col_idx must be int32 [nnz]")
+    scores = None
+    if return_scores:
+        d = plan.desc
+        scores = torch.empty((d["batch"], d["heads"], inf["nqb"], inf["nkb"]),
+                             dtype=torch.float64, device=dev)
+    qv, kv = tensor_view(q), tensor_view(k)
+    st = _lib.lcsa_select_noalloc(plan.handle, ctypes.byref(qv), ctypes.byref(kv),
+                                  row_ptr.data_ptr(), col_idx.data_ptr() if inf["nnz"] else None,
+                                  scores.data_ptr() if scores is not None else None,
+                                  _stream_ptr(q, stream))
+    _check(st, "lcsa_select_noalloc")
     if return_scores:
         return row_ptr, col_idx, scores
     return row_ptr, col_idx

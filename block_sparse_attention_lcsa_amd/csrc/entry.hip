@@ -344,6 +344,36 @@ lcsa_status threshold_select_impl(const char* fn, lcsa_plan_t plan, const lcsa_t
                      q_rot, k_rot, d_kth, d_tau);
 }
 
+// Workspace of lcsa_select_noalloc: one array per device, in the library's
+// device code object, held until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, not a device address; the device
+// address is looked up per device (scratch_address) and only that address
+// is handed to kernels.
+static __device__ __align__(256) double scratch[LCSA_SELECT_NOALLOC_MAX_BYTES / sizeof(double)];
+
+namespace {
+
+// Device address of the current device's scratch array, looked up once per
+// device with that device current.
+lcsa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256)
+    return fail(LCSA_ERR_DEVICE, "no current HIP device");
+  static std::mutex mu;
+  static void* addr[256] = {nullptr};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(LCSA_ERR_DEVICE, "scratch array of device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return LCSA_OK;
+}
+
+}  // namespace
 }  // namespace lcsa
 
 using lcsa::fail;
@@ -356,6 +386,27 @@ lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   lcsa::clear_error();
   return lcsa::select_impl("lcsa_select", plan, q, k, nullptr, 0, nullptr, d_row_ptr, d_col_idx,
                            d_scores, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_select_noalloc(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                                int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                                void* stream) {
+  lcsa::clear_error();
+  if (!plan) return fail(LCSA_ERR_NULL, "lcsa_select_noalloc: plan is NULL");
+  if (plan->info.select_workspace_bytes > LCSA_SELECT_NOALLOC_MAX_BYTES)
+    return fail(LCSA_ERR_WORKSPACE,
+                "lcsa_select_noalloc: the plan needs %llu workspace bytes, above the %llu of the "
+                "library's scratch array; use lcsa_select with a caller workspace",
+                (unsigned long long)plan->info.select_workspace_bytes,
+                (unsigned long long)LCSA_SELECT_NOALLOC_MAX_BYTES);
+  lcsa_status st;
+  if ((st = lcsa::check_device())) return st;
+  void* ws = nullptr;
+  if ((st = lcsa::scratch_address(&ws))) return st;
+  // Every entry of the workspace that select reads, pool writes first in
+  // the same call, so the array needs no clearing between calls.
+  return lcsa::select_impl("lcsa_select_noalloc", plan, q, k, nullptr, 0, nullptr, d_row_ptr,
+                           d_col_idx, d_scores, ws, LCSA_SELECT_NOALLOC_MAX_BYTES, stream);
 }
 
 lcsa_status lcsa_select_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,

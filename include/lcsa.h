@@ -202,6 +202,27 @@ lcsa_status lcsa_select(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
                         int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
                         void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* Block selection that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments
+ * (less the workspace) and same result as lcsa_select; the pooled vectors go
+ * to a scratch array inside the library instead, of
+ * LCSA_SELECT_NOALLOC_MAX_BYTES bytes on each device the library runs on,
+ * held until the process ends.  The call itself allocates nothing.
+ *  - A plan whose select_workspace_bytes exceeds
+ *    LCSA_SELECT_NOALLOC_MAX_BYTES is rejected with LCSA_ERR_WORKSPACE
+ *    before anything is enqueued (48 MiB holds the 184320-token 4K first
+ *    chunk at 12 heads, 33.75 MiB).
+ *  - All calls on one device share that device's one array: calls that
+ *    overlap in time on one device (other streams, other host threads)
+ *    race on it, and the caller must serialise them.  Each call writes every
+ *    entry it later reads, so nothing carries over from an earlier call.
+ * Errors: as lcsa_select (WORKSPACE only for the size limit). */
+#define LCSA_SELECT_NOALLOC_MAX_BYTES (48ull << 20)
+lcsa_status lcsa_select_noalloc(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                                int32_t* d_row_ptr, int32_t* d_col_idx, double* d_scores,
+                                void* stream);
+
 /* Block-sparse attention forward: for each CSR row (b, h, query block) and
  * every token of every key block in the row, z = scale * q.k; online softmax
  * over those tokens; O = sum softmax(z) v, rounded to bf16 (nearest even);

@@ -335,3 +335,22 @@ def test_threshold_entry_point_validation_statuses():
     assert steady(rope=bad_rope) == 2                                # rope checked when given
     if not torch.cuda.is_available():
         assert steady() == 6 and reuse() == 6 and reuse(ring=ok_ring) == 6   # DEVICE
+
+
+def test_noalloc_select_statuses():
+    """lcsa_select_noalloc refuses a NULL plan and a plan whose workspace
+    exceeds the library's scratch array before any HIP call."""
+    lib = lcsa._lib
+    assert lib.lcsa_select_noalloc(None, None, None, None, None, None, None) == 1
+    big = lcsa.Plan.from_desc(dict(li.CONFIGS["first_2048x3840"], batch=2))
+    assert big.info["select_workspace_bytes"] > lcsa.SELECT_NOALLOC_MAX_BYTES
+    bq, bk = _fake_view(plan=big), _fake_view(plan=big, tokens="kv")
+    assert lib.lcsa_select_noalloc(big.handle, ctypes.byref(bq), ctypes.byref(bk), 0x20000,
+                                   0x30000, None, None) == 5                 # WORKSPACE
+    assert "scratch" in lib.lcsa_last_error().decode()
+    p4k = lcsa.Plan.from_desc(li.CONFIGS["first_2048x3840"])
+    assert p4k.info["select_workspace_bytes"] <= lcsa.SELECT_NOALLOC_MAX_BYTES
+    if not torch.cuda.is_available():
+        good = _fake_view()
+        assert lib.lcsa_select_noalloc(_TINY.handle, ctypes.byref(good), ctypes.byref(good),
+                                       0x20000, 0x30000, None, None) == 6    # DEVICE
