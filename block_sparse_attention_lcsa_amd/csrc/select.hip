@@ -80,8 +80,9 @@ __device__ inline uint32_t rope_pair(uint32_t w, float2 cs) {
   return bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
 }
 
-// grid (NQB + pooled key blocks, heads, batch): x < NQB pools query block x,
-// otherwise key block x - NQB of the KV-window frames k_first onwards, read
+// grid ((NQB + pooled key blocks) x heads, 1, batch): block index x / heads
+// (head x % heads) < NQB pools that query block, otherwise key block
+// x / heads - NQB of the KV-window frames k_first onwards, read
 // from (and stored for) their storage frame kv_slot[t].  Thread (c, tg) sums
 // channels 8c..8c+7 of tokens tg, tg+16, ...  With ROPE each 16-byte slice
 // (channel pairs 4c..4c+3) is first turned by the rotary tables, written to
@@ -90,9 +91,13 @@ template <int BT, bool ROPE>
 __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
   __shared__ double red[16 * 128];
   const GridGeom& g = p.g;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const bool is_q = (int)blockIdx.x < g.nqb;
-  const int blk = is_q ? (int)blockIdx.x : (int)blockIdx.x - g.nqb + p.k_first * g.nbf;
+  // heads vary fastest along the grid, so the workgroups of one block's
+  // heads, which read neighbouring 256-byte slices of the same token rows,
+  // are dispatched together
+  const int h = (int)(blockIdx.x % (unsigned)g.heads), b = blockIdx.z;
+  const int xb = (int)(blockIdx.x / (unsigned)g.heads);
+  const bool is_q = xb < g.nqb;
+  const int blk = is_q ? xb : xb - g.nqb + p.k_first * g.nbf;
   const View& x = is_q ? p.q : p.k;
   const int t = blk / g.nbf, pos = blk - t * g.nbf;
   const int by = pos / g.nbw, bx = pos - by * g.nbw;
@@ -426,7 +431,7 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
 
 hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, bool rope,
                        hipStream_t stream) {
-  const dim3 grid(p.g.nqb + (p.g.kv_frames - p.k_first) * p.g.nbf, p.g.heads, batch);
+  const dim3 grid((p.g.nqb + (p.g.kv_frames - p.k_first) * p.g.nbf) * p.g.heads, 1, batch);
   if (block_tokens == 128) {
     if (rope)
       hipLaunchKernelGGL((pool_kernel<128, true>), grid, dim3(kPoolThreads), 0, stream, p);

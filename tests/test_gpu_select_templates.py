@@ -1,7 +1,8 @@
 """Select parity on small grids chosen to reach every compiled width of the
 select kernel: window candidates per lane M in {1, 2, 3, 4, 6, 8, 12, 16}
 and query frames per workgroup R in {1, 2, 4, 6, 8}, including a partly
-filled last frame group and more rows than waves.  Scores must match the
+filled last frame group, more rows than waves and the largest window the
+kernel takes (1024 candidates, with k = 300 and k = 1023).  Scores must match the
 float64 oracle to 1e-12 of the row scale and masks must be identical except
 at near-ties, as in test_gpu_parity.py."""
 import numpy as np
@@ -27,6 +28,9 @@ def _desc(q_frames, cached, kv_ratio, nb, local_range, topk):
 # (label, desc, expected M, expected R)
 CASES = [
     ("m16_r8", _desc(8, 0, 1.0, 11, 11, 50), 16, 8),     # 8 KV frames x 11x11 = 968 candidates
+    # the largest window the select kernel takes: 16 KV frames x 8x8 = 1024
+    ("m16_full_window", _desc(8, 8, 2.0, 8, 15, 300), 16, 8),
+    ("m16_full_window_all_but_one", _desc(8, 8, 2.0, 8, 15, 1023), 16, 8),
     ("m12_r4", _desc(4, 2, 1.5, 11, 11, 60), 12, 4),     # 6 x 121 = 726
     ("m8_r2", _desc(2, 2, 2.0, 11, 11, 40), 8, 2),       # 4 x 121 = 484
     ("m6_r1", _desc(1, 2, 3.0, 11, 11, 30), 6, 1),       # 3 x 121 = 363
