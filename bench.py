@@ -9,8 +9,12 @@ seeded synthetic bf16 inputs resident in HBM before timing starts.
 
 Prints ONE JSON line.  value = useful attention TFLOP/s of the whole step
 (useful FLOP = 4 * 128 * 128 * 128 per selected block pair; skipped blocks do
-not count), ms_per_step = select+attend ms per chunk.  roofline = the attend
-kernel (MFMA-bound) timed with HIP events on its stream; select_roofline =
+not count), ms_per_step = select+attend ms per chunk, from --steps steps run
+back to back with no event between kernels.  roofline = the attend kernel
+(MFMA-bound) timed with HIP events on its stream over a second pass of as
+many steps, each with events around select and attend.  Before the --warmup
+steps, steps run back to back for SPIN_UP_S seconds (spin_up_steps) so that
+the GPU's clocks leave the idle of input generation; select_roofline =
 the select entry point (pool + select kernels) against HBM bandwidth;
 cpu_baseline = the float64 CPU oracle on the same step, its heads spread
 over worker processes (1 warm-up and 3 timed runs, medians); parity = the
@@ -42,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+SPIN_UP_S = 0.25                 # back-to-back steps before the warm-up steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
 ATTEND_SRC = os.path.join(ROOT, "block_sparse_attention_lcsa_amd", "csrc", "attend.hip")
 
@@ -323,26 +328,49 @@ def main():
         if ev:
             ev[2].record(stream)
 
+    # Spin-up: the GPU has idled through input generation, and the first few
+    # tens of back-to-back steps after that run a few per cent slow and
+    # unevenly (up to 9 % in A/B passes of 20 steps) before its clocks settle.
+    # Steps are run until SPIN_UP_S of wall time has passed, then the W
+    # warm-up steps, then the timed ones.
+    spin_steps = 0
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < SPIN_UP_S:
+        for _ in range(10):
+            step()
+        spin_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The timed steps: nothing between the kernels of one step or between
+    # steps.  A timing event recorded on the stream costs the GPU an idle
+    # gap of about 6-10 us before the next kernel (seen in kernel traces),
+    # so the per-kernel events are recorded in a second pass of as many
+    # steps, right after this one.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    gpu_ms = t_start.elapsed_time(t_end) / args.steps
 
+    # Per-kernel breakdown: events before select, between select and attend
+    # and after attend, on the stream the kernels run on.  The attend window
+    # holds the event gap before attend, so it reads slightly high.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
     att_ms = [e[1].elapsed_time(e[2]) for e in evs]
     both_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    gpu_ms = t_start.elapsed_time(t_end) / args.steps
 
     # Cold caches: before each of these steps a fill kernel writes 512 MiB,
     # which evicts every XCD's L2 and the memory-side cache; the flush is
@@ -388,8 +416,13 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             g_out = graph_body()
-        for _ in range(10):      # the first replays of a new graph run slower
-            g.replay()
+        # the first replays of a new graph run slower, and the cold-cache
+        # steps before left the GPU idle between flushes: spin up as above
+        t_spin = time.perf_counter()
+        while time.perf_counter() - t_spin < SPIN_UP_S:
+            for _ in range(10):
+                g.replay()
+            torch.cuda.synchronize()
         gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         gev[0].record(stream)
@@ -496,6 +529,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spin_up_steps": spin_steps,
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -567,9 +601,11 @@ def main():
 
 
 def time_workloads(names, seed, dev, stream):
-    """Select and attend medians of the other named workloads, timed with
-    HIP events on the launch stream in this same run (10 warm-up steps, then
-    20 timed; 10 at the 184320-token chunk)."""
+    """Step time and select / attend medians of the other named workloads,
+    timed with HIP events on the launch stream in this same run: a spin-up
+    of SPIN_UP_S seconds and 10 warm-up steps, then 20 steps back to back (10
+    at the 184320-token chunk) for the step time, then as many with events
+    around select and attend."""
     import numpy as np
     import torch
     import block_sparse_attention_lcsa_amd as lcsa
@@ -599,12 +635,25 @@ def time_workloads(names, seed, dev, stream):
             lcsa.attend(plan, q, k, v, rp, ci, out=o, workspace=att_ws)
             if ev:
                 ev[2].record(stream)
+        # spin-up after the idle of input generation, as for the main workload
+        t_spin = time.perf_counter()
+        while time.perf_counter() - t_spin < SPIN_UP_S:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
         for _ in range(10):
             step()
+        # n steps back to back (the step time), then n with per-kernel events
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(n):
+            step()
+        t1.record(stream)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         for e in evs:
             step(e)
         torch.cuda.synchronize()
+        step_ms = t0.elapsed_time(t1) / n
         sel = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
         att = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
         both = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
@@ -621,7 +670,8 @@ def time_workloads(names, seed, dev, stream):
             "attend_frac_of_bf16_peak": flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "select_gbs": sel_bytes / (sel * 1e-3) / 1e9,
             "select_frac_of_hbm": sel_bytes / (sel * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "step_tflops": flops / (both * 1e-3) / 1e12,
+            "step_ms": step_ms,
+            "step_tflops": flops / (step_ms * 1e-3) / 1e12,
         }
         print(f"bench: {name} select {sel:.4f} ms, attend {att:.4f} ms", file=sys.stderr, flush=True)
         del q, k, v, o, ws, att_ws, inp
