@@ -77,3 +77,48 @@ def test_noalloc_binding_and_size_limit():
         lcsa._check(lcsa._lib.lcsa_select_noalloc(big.handle, None, None, None, None, None, None),
                     "lcsa_select_noalloc")
     assert ei.value.name == "LCSA_ERR_WORKSPACE"
+
+
+def test_noalloc_select_in_a_graph():
+    """The callers the call is for: a chunk captured in a HIP graph with
+    lcsa_select_noalloc into static CSR buffers, then attention, replayed on
+    new inputs with eager calls between replays; each replay must equal
+    eager lcsa_select + lcsa_attend on the same inputs bit for bit."""
+    desc, q0, k0, v0 = device_qkv("stream_768x1280", seed=0)
+    plan = lcsa.Plan.from_desc(desc)
+    inf = plan.info
+    q, k, v = q0.clone(), k0.clone(), v0.clone()
+    rp = torch.empty(inf["rows"] + 1, dtype=torch.int32, device="cuda")
+    ci = torch.empty(inf["nnz"], dtype=torch.int32, device="cuda")
+    att_ws = torch.empty(int(inf["attend_workspace_bytes"]), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def chunk():
+        lcsa.select_noalloc(plan, q, k, row_ptr=rp, col_idx=ci)
+        lcsa.attend(plan, q, k, v, rp, ci, out=out, workspace=att_ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            chunk()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chunk()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 0, 1):
+        _, qs, ks, vs = device_qkv("stream_768x1280", seed=seed)
+        q.copy_(qs)
+        k.copy_(ks)
+        v.copy_(vs)
+        g.replay()
+        torch.cuda.synchronize()
+        got_ci, got_out = ci.clone(), out.clone()
+        rp_e, ci_e = lcsa.select(plan, qs, ks)
+        out_e = lcsa.attend(plan, qs, ks, vs, rp_e, ci_e)
+        torch.cuda.synchronize()
+        assert torch.equal(rp, rp_e) and torch.equal(got_ci, ci_e), f"seed {seed}: CSR differs"
+        assert torch.equal(got_out, out_e), f"seed {seed}: attention output differs"
+        say(f"  replay on seed {seed}: CSR and output equal to eager calls")
