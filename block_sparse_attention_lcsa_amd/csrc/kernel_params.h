@@ -47,13 +47,14 @@ struct RopeParams {
   OutView q_rot, k_rot;  // rotated Q and K (bf16), written by the pool kernel
 };
 
-// Pooled K lives per storage frame, channel pairs innermost:
-// kcache[slot][B*H][64][NBF][2] holds channel 2c + e of position p at [c][p][e].
+// Pooled K lives per storage frame, in groups of 8 positions:
+// kcache[slot][B*H][NBF / 8 rounded up][64][8][2] holds channel 2c + e of
+// position p at [p / 8][c][p % 8][e].
 struct PoolParams {
   GridGeom g;
   View q, k;
   double* qbar;          // [B][H][NQB][128]
-  double* kcache;        // [slots][B*H][64][NBF][2]
+  double* kcache;        // [slots][B*H][ceil(NBF / 8)][64][8][2]
   int32_t k_first;       // first KV-window frame whose K blocks are pooled
   RopeParams rope;       // used by the rotary variant of the pool kernel only
 };
@@ -61,7 +62,7 @@ struct PoolParams {
 struct SelectParams {
   GridGeom g;
   const double* qbar;    // [B][H][NQB][128]
-  const double* kcache;  // [slots][B*H][64][NBF][2]
+  const double* kcache;  // [slots][B*H][ceil(NBF / 8)][64][8][2]
   int32_t batch;
   int32_t* row_ptr;
   int32_t* col_idx;

@@ -195,16 +195,18 @@ lcsa_status lcsa_plan_create(const lcsa_desc* d, lcsa_plan_t* out) {
   in.max_window = mxw;
   in.nnz = nnz;
   in.useful_flops = 4.0 * 128.0 * in.block_tokens * in.block_tokens * static_cast<double>(nnz);
-  // Workspace: pooled Q [B][H][NQB][128] then pooled K transposed per
-  // (b, h) [B][H][128][NKB], both float64.
+  // Pooled K per frame slot: [B*H][ceil(NBF / 8)][64 channel pairs][8][2]
+  // float64.  Select workspace: pooled Q [B][H][NQB][128] float64, then
+  // one such slot per KV-window frame.
+  in.kcache_slot_bytes = static_cast<uint64_t>(d->batch) * d->heads * 128ull *
+                         static_cast<uint64_t>((nbf + 7) / 8 * 8) * 8ull;
   in.select_workspace_bytes = static_cast<uint64_t>(d->batch) * d->heads * 128ull *
-                              static_cast<uint64_t>(nqb + nkb) * 8ull;
+                                  static_cast<uint64_t>(nqb) * 8ull +
+                              static_cast<uint64_t>(in.kv_frames) * in.kcache_slot_bytes;
   // Attend: at most one partly filled round of split pieces, i.e. as many
   // pieces as workgroups fit on the largest gfx950 device at once.
   const uint64_t bt = static_cast<uint64_t>(in.block_tokens);
   in.attend_workspace_bytes = lcsa::kMaxCus * (8 / (bt / 32)) * bt * (128 + 2) * 4;
-  in.kcache_slot_bytes = static_cast<uint64_t>(d->batch) * d->heads * 128ull *
-                         static_cast<uint64_t>(nbf) * 8ull;
 
   try {
     p->row_ptr.resize(static_cast<size_t>(rows) + 1);

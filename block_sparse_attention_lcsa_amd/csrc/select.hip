@@ -185,7 +185,8 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
     if (is_q)
       p.qbar[(bh * g.nqb + blk) * 128 + tid] = s;
     else
-      p.kcache[((((int64_t)tf * gridDim.z * g.heads + bh) * 64 + (tid >> 1)) * g.nbf + pos) * 2 + (tid & 1)] = s;
+      p.kcache[((((int64_t)tf * gridDim.z * g.heads + bh) * ((g.nbf + 7) >> 3) + (pos >> 3)) * 64 +
+                (tid >> 1)) * 16 + (pos & 7) * 2 + (tid & 1)] = s;
   }
 }
 
@@ -229,14 +230,51 @@ struct DeviceWave {
   }
 };
 
+// Workgroup barrier that completes this wave's own LDS operations but leaves
+// its in-flight global loads running (a plain __syncthreads would wait for
+// them too).
+__device__ inline void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// g.kv_slot[t] for a per-lane t that does not decrease from lane to lane.
+// When the wave's frames span at most 4 (a window's candidates run through
+// a few frames), four scalar loads cover them; a per-lane load of the table
+// would be a vector-memory round trip ahead of the first pooled-K load.
+__device__ inline int frame_slot(const GridGeom& g, int t) {
+  const int t_lo = __builtin_amdgcn_readfirstlane(t);
+  const int t_hi = __builtin_amdgcn_readlane(t, 63);
+  if (t_hi - t_lo < 4) {
+    int slot = g.kv_slot[t_lo];
+#pragma unroll
+    for (int c = 1; c < 4; ++c) {
+      const int sc = g.kv_slot[min(t_lo + c, kMaxKvFrames - 1)];
+      slot = t == t_lo + c ? sc : slot;
+    }
+    return slot;
+  }
+  return g.kv_slot[t];
+}
+
+// Scoring waves of a workgroup whose rows have up to 64 M window candidates,
+// and candidates per scoring lane.
+template <int M>
+struct ScoreShape {
+  static constexpr int waves = kSelectWaves;
+  static constexpr int slots = (M + waves - 1) / waves;
+};
+
 // One workgroup takes the rows of up to R query frames at one spatial
-// position; they share the window.  Scores: wave w computes window
-// candidates e = lane + 64 (4 j + w) of every row into an LDS table, so each
-// pooled-key load feeds R dot products.  Top-k: wave w then takes rows w,
-// w + 4, ... and reads candidate e = lane + 64 j (j < M) of its row.
+// position; they share the window.  Scores: scoring wave w < SW computes
+// window candidates e = lane + 64 (SW j + w) of every row into an LDS table,
+// so each pooled-key load feeds R dot products.  Top-k: wave w then takes
+// rows w, w + 4, ... and reads candidate e = lane + 64 j (j < M) of its row.
 template <int M, int R>
 __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams p) {
-  constexpr int MW = (M + kSelectWaves - 1) / kSelectWaves;   // scoring slots per lane
+  constexpr int SW = ScoreShape<M>::waves;
+  constexpr int MW = ScoreShape<M>::slots;   // scoring slots per lane
   __shared__ double qs[R][128];
   __shared__ double sc[R][64 * M];
   const GridGeom& g = p.g;
@@ -249,78 +287,127 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   const int by = pos / g.nbw, bx = pos - by * g.nbw;
   const WindowBox w = window_box(g, by, bx);
   const int64_t bh = (int64_t)b * g.heads + h;
+  const bool scoring = wave < SW && 64 * wave < w.n;
 
-  // Pooled queries of the rows -> LDS (read back as broadcasts).
-  for (int i = tid; i < nr * 128; i += kSelectWaves * 64)
-    qs[i >> 7][i & 127] = p.qbar[(bh * g.nqb + (int64_t)(tq0 + (i >> 7)) * g.nbf + pos) * 128 + (i & 127)];
-  __syncthreads();
-
-  // Float64 scores.  Channels d, d + 1 (d even) of the pooled K of key block
-  // (t, pos') sit together at kcache[kv_slot[t]][bh][d / 2][pos'][0..1], so
-  // a lane reads two channels per 16-byte load and neighbouring lanes
-  // (neighbouring positions) read neighbouring 16 bytes.
-  if (64 * wave < w.n) {
-    int64_t koff[MW];
-    bool valid[MW];
-    double acc[MW][R];
+  // Float64 scores.  The pooled K of key block (t, pos') sits in its frame
+  // slot's group of 8 positions, pos' / 8, as 64 channel pairs of 8
+  // positions: pair dp of the block is 128 bytes after pair dp - 1, so a
+  // lane addresses every pair of its candidate from one pointer with a
+  // constant offset, and the 8 lanes of neighbouring positions read one
+  // 128-byte line per pair.
+  //
+  // Two levels of prefetch, so that loads are in flight while FMAs run:
+  //  - pooled-K pairs in batches of kD, double-buffered: batch i + 1 is
+  //    loaded before the FMAs of batch i (batch 0 before the pooled queries
+  //    reach LDS, so that both loads overlap);
+  //  - the pooled queries of pair dp + QL are read from LDS before the FMAs
+  //    of pair dp.
+  // The compiler sees all of these loads as free to move, and hoisting them
+  // together exhausts the registers (it spills), so their addresses are made
+  // to depend on the scores: batch i + 1 on every score after batch i - 1,
+  // the queries of pair dp + QL on every score after pair dp - 1.  The FMA
+  // order is dp ascending for every score.
+  constexpr int kD = MW == 1 ? 8 : MW == 2 ? 4 : 2;
+  constexpr int kNB = 64 / kD;
+  constexpr int QL = MW == 1 ? 3 : 1;   // QL + 1 divides 2 kD: buffer indices stay constant
+  // Candidates of the lane's scoring slots (lanes past the window take the
+  // window's last candidate: in-bounds loads, scores never used), then the
+  // loads: pooled queries first, so that waiting for them does not wait for
+  // the pooled K, then pooled-K batch 0.  Every wave issues them, so that no
+  // branch joins before the waits (which would make them wait for all).
+  const double2* kp[MW];
+  double2 buf0[kD][MW], buf1[kD][MW];
+  double acc[MW][R];
+  {
     const int64_t bh_all = (int64_t)p.batch * g.heads;
+    const int64_t groups = (g.nbf + 7) >> 3;
+    const double2* kd = reinterpret_cast<const double2*>(p.kcache);
 #pragma unroll
     for (int j = 0; j < MW; ++j) {
-      const int e = lane + 64 * (kSelectWaves * j + wave);
-      valid[j] = e < w.n;
-      const int kb = valid[j] ? window_kb(g, w, e) : 0;
-      const int t = kb / g.nbf;
-      koff[j] = ((int64_t)g.kv_slot[t] * bh_all + bh) * 64 * g.nbf + (kb - t * g.nbf);   // in pairs
+      const int e = min(lane + 64 * (SW * j + wave), w.n - 1);
+      const int kb = window_kb(g, w, e);
+      const int t = kb / g.nbf, kpos = kb - t * g.nbf;
+      const int slot = frame_slot(g, t);
+      kp[j] = kd + (((int64_t)slot * bh_all + bh) * groups + (kpos >> 3)) * 512 + (kpos & 7);
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[j][r] = 0.0;
     }
-    const double2* kd = reinterpret_cast<const double2*>(p.kcache);
-    if constexpr (MW == 1) {
-      // One candidate per lane: latency-bound.  Channel pairs go in steps of
-      // kU, and the loads of step i + 1 are issued before the FMAs of step i,
-      // so a load latency overlaps a step of arithmetic (same FMA order).
-      constexpr int kU = 4;
-      double2 cur[kU], nxt[kU];
+  }
+  // (rows past the last query frame load the last frame's row, unused)
+  double qreg[(R * 128 + kSelectWaves * 64 - 1) / (kSelectWaves * 64)];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) cur[u] = kd[(int64_t)u * g.nbf + koff[0]];
+  for (int u = 0; u < (int)(sizeof(qreg) / sizeof(double)); ++u) {
+    const int i = min(tid + u * kSelectWaves * 64, R * 128 - 1);
+    const int tq = min(tq0 + (i >> 7), g.q_frames - 1);
+    qreg[u] = p.qbar[(bh * g.nqb + (int64_t)tq * g.nbf + pos) * 128 + (i & 127)];
+  }
 #pragma unroll
-      for (int dp0 = 0; dp0 < 64; dp0 += kU) {
-        if (dp0 + kU < 64) {
+  for (int u = 0; u < kD; ++u)
 #pragma unroll
-          for (int u = 0; u < kU; ++u) nxt[u] = kd[(int64_t)(dp0 + kU + u) * g.nbf + koff[0]];
+    for (int j = 0; j < MW; ++j) buf0[u][j] = kp[j][u * 8];
+#pragma unroll
+  for (int u = 0; u < (int)(sizeof(qreg) / sizeof(double)); ++u) {
+    const int i = tid + u * kSelectWaves * 64;
+    // only a last, partial round needs the test
+    if ((u + 1) * kSelectWaves * 64 <= R * 128 || i < R * 128) qs[i >> 7][i & 127] = qreg[u];
+  }
+  barrier_lds();
+
+  if (scoring) {
+    double2 qv[QL + 1][R];
+    const double2* q2 = reinterpret_cast<const double2*>(&qs[0][0]);   // [R][64]
+    // always 0; they carry the dependencies of the pooled-K loads and the
+    // query reads (an integer, so that the pointers keep their address space)
+    int ko = 0, qo = 0;
+#pragma unroll
+    for (int l = 0; l < QL; ++l)
+#pragma unroll
+      for (int r = 0; r < R; ++r) qv[l][r] = q2[r * 64 + l];
+    // one batch: load batch bi + 1 into nxt, then the FMAs of batch bi
+    auto batch = [&](int bi, const double2 (&cur)[kD][MW], double2 (&nxt)[kD][MW]) {
+      if (bi + 1 < kNB) {
+        if (bi > 0) {
+#pragma unroll
+          for (int j = 0; j < MW; ++j)
+#pragma unroll
+            for (int r = 0; r < R; ++r) asm volatile("" : "+v"(ko) : "v"(acc[j][r]));
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int dp = dp0 + u;
+        for (int u = 0; u < kD; ++u)
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const double q0 = qs[r][2 * dp], q1 = qs[r][2 * dp + 1];
-            acc[0][r] = fma(q1, cur[u].y, fma(q0, cur[u].x, acc[0][r]));
-          }
-        }
-        if (dp0 + kU < 64) {
-#pragma unroll
-          for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
-        }
+          for (int j = 0; j < MW; ++j) nxt[u][j] = kp[j][ko + ((bi + 1) * kD + u) * 8];
       }
-    } else {
-#pragma unroll 2
-      for (int dp = 0; dp < 64; ++dp) {
-        double2 kv[MW];
 #pragma unroll
-        for (int j = 0; j < MW; ++j) kv[j] = kd[(int64_t)dp * g.nbf + koff[j]];
+      for (int u = 0; u < kD; ++u) {
+        const int dp = bi * kD + u;
+        if (dp + QL < 64) {
+          if (dp > 0) {
+#pragma unroll
+            for (int j = 0; j < MW; ++j)
+#pragma unroll
+              for (int r = 0; r < R; ++r) asm volatile("" : "+v"(qo) : "v"(acc[j][r]));
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) qv[(u + QL) % (QL + 1)][r] = q2[qo + r * 64 + dp + QL];
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const double q0 = qs[r][2 * dp], q1 = qs[r][2 * dp + 1];
+          const double2 qq = qv[u % (QL + 1)][r];
 #pragma unroll
-          for (int j = 0; j < MW; ++j) acc[j][r] = fma(q1, kv[j].y, fma(q0, kv[j].x, acc[j][r]));
+          for (int j = 0; j < MW; ++j)
+            acc[j][r] = fma(qq.y, cur[u][j].y, fma(qq.x, cur[u][j].x, acc[j][r]));
         }
       }
+    };
+#pragma unroll
+    for (int bi = 0; bi < kNB; bi += 2) {
+      batch(bi, buf0, buf1);
+      batch(bi + 1, buf1, buf0);
     }
 #pragma unroll
     for (int j = 0; j < MW; ++j) {
-      if (valid[j]) {
-        const int e = lane + 64 * (kSelectWaves * j + wave);
+      const int e = lane + 64 * (SW * j + wave);
+      if (e < w.n) {
 #pragma unroll
         for (int r = 0; r < R; ++r) sc[r][e] = acc[j][r];
       }
@@ -463,6 +550,11 @@ void launch_select_m(const SelectParams& p, int batch, hipStream_t stream) {
     launch_select_mr<M, (RMAX < 2 ? RMAX : 2)>(p, batch, stream);
   else if (qf <= 4 || RMAX <= 4)
     launch_select_mr<M, (RMAX < 4 ? RMAX : 4)>(p, batch, stream);
+  else if (M <= 4 && qf <= 6)
+    // narrow windows: two workgroups of 3 rows instead of one of 6, so twice
+    // the waves hide the latency of the scoring loop and every row's top-k
+    // runs in one round (14.6 against 15.4 us at the first 768x1280 chunk)
+    launch_select_mr<M, 3>(p, batch, stream);
   else if (qf <= 6 || RMAX <= 6)
     launch_select_mr<M, (RMAX < 6 ? RMAX : 6)>(p, batch, stream);
   else

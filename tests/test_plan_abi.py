@@ -75,7 +75,10 @@ def test_plan_matches_oracle_geometry(name):
     # room for one device-wide round of split pieces: 256 CUs x 8 waves
     bt = g.block_tokens
     assert inf["attend_workspace_bytes"] == 256 * (8 // (bt // 32)) * bt * (128 + 2) * 4
-    assert inf["kcache_slot_bytes"] == g.batch * g.heads * 128 * g.nbf * 8
+    # pooled K per frame slot, positions in groups of 8 (the last padded)
+    assert inf["kcache_slot_bytes"] == g.batch * g.heads * 128 * (-(-g.nbf // 8) * 8) * 8
+    assert inf["select_workspace_bytes"] == (g.batch * g.heads * 128 * g.nqb * 8
+                                             + g.kv_frames * inf["kcache_slot_bytes"])
     for qb in range(0, g.nqb, max(1, g.nqb // 37)):
         assert np.array_equal(p.window(qb), oracle.window(g, qb))
 
