@@ -312,6 +312,18 @@ def main():
             return lcsa.select_rope(p, q, k, rtab, q_rot=q_rot, k_rot=k_rot, workspace=ws)[2:]
         return lcsa.select(p, q, k, workspace=ws)
 
+    def do_attend(p, rp, ci):
+        # a reused-threshold CSR has rows of many lengths: longest first
+        if args.reuse:
+            return lcsa.attend_varlen(p, q, k_ring if args.ring else k, v_ring if args.ring else v,
+                                      rp, ci, out=out, workspace=att_ws,
+                                      ring=ring if args.ring else None)
+        if args.ring:
+            return lcsa.attend_ring(p, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
+        if args.rope:
+            return lcsa.attend(p, q_rot, k_rot, v, rp, ci, out=out, workspace=att_ws)
+        return lcsa.attend(p, q, k, v, rp, ci, out=out, workspace=att_ws)
+
     def step(ev=None):
         p = lcsa.Plan.from_desc(desc)                      # host plan (per shape)
         if ev:
@@ -319,12 +331,7 @@ def main():
         rp, ci = do_select(p)
         if ev:
             ev[1].record(stream)
-        if args.ring:
-            lcsa.attend_ring(p, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
-        elif args.rope:
-            lcsa.attend(p, q_rot, k_rot, v, rp, ci, out=out, workspace=att_ws)
-        else:
-            lcsa.attend(p, q, k, v, rp, ci, out=out, workspace=att_ws)
+        do_attend(p, rp, ci)
         if ev:
             ev[2].record(stream)
 
@@ -399,12 +406,7 @@ def main():
 
         def graph_body():
             rp, ci = do_select(gplan)
-            if args.ring:
-                lcsa.attend_ring(gplan, q, k_ring, v_ring, ring, rp, ci, out=out, workspace=att_ws)
-            elif args.rope:
-                lcsa.attend(gplan, q_rot, k_rot, v, rp, ci, out=out, workspace=att_ws)
-            else:
-                lcsa.attend(gplan, q, k, v, rp, ci, out=out, workspace=att_ws)
+            do_attend(gplan, rp, ci)
             return rp, ci
 
         side = torch.cuda.Stream(dev)
@@ -505,6 +507,8 @@ def main():
             "select_top_k_ms_median": tmed(lambda: lcsa.select(rplan, q, k, workspace=ws)),
             "attend_reused_mask_ms_median": tmed(
                 lambda: lcsa.attend(rplan, q, k, v, rp_r, ci_r, out=o_r, workspace=att_ws)),
+            "attend_varlen_reused_mask_ms_median": tmed(
+                lambda: lcsa.attend_varlen(rplan, q, k, v, rp_r, ci_r, out=o_r, workspace=att_ws)),
             "attend_top_k_mask_ms_median": tmed(
                 lambda: lcsa.attend(rplan, q, k, v, rp_t, ci_t, out=o_t, workspace=att_ws)),
         }

@@ -19,7 +19,7 @@ import ctypes
 import os
 
 __all__ = ["Plan", "LcsaError", "select", "select_noalloc", "attend", "select_ring", "attend_ring", "select_rope",
-           "select_ring_rope", "rope", "select_steady", "select_reuse", "lib_path", "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
+           "select_ring_rope", "rope", "select_steady", "select_reuse", "attend_varlen", "lib_path", "abi_version", "EXPORTS", "MAX_KV_FRAMES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -47,7 +47,7 @@ EXPORTS = [
     "lcsa_plan_create", "lcsa_plan_destroy", "lcsa_plan_get_info", "lcsa_plan_row_ptr",
     "lcsa_plan_window", "lcsa_select", "lcsa_attend", "lcsa_select_rope",
     "lcsa_select_ring_rope", "lcsa_select_ring", "lcsa_attend_ring", "lcsa_select_steady",
-    "lcsa_select_reuse", "lcsa_select_noalloc",
+    "lcsa_select_reuse", "lcsa_select_noalloc", "lcsa_attend_varlen",
     "lcsa_status_string", "lcsa_last_error", "lcsa_abi_version",
 ]
 SELECT_NOALLOC_MAX_BYTES = 48 << 20
@@ -145,6 +145,11 @@ _lib.lcsa_attend_ring.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER
                                   ctypes.c_int64, ctypes.POINTER(LcsaTensor), _P, _P,
                                   ctypes.c_size_t, _P]
 _lib.lcsa_attend_ring.restype = ctypes.c_int32
+_lib.lcsa_attend_varlen.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
+                                    ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaKvRing), _P, _P,
+                                    ctypes.c_int64, ctypes.POINTER(LcsaTensor), _P, _P,
+                                    ctypes.c_size_t, _P]
+_lib.lcsa_attend_varlen.restype = ctypes.c_int32
 _lib.lcsa_select_steady.argtypes = [_P, ctypes.POINTER(LcsaTensor), ctypes.POINTER(LcsaTensor),
                                     ctypes.POINTER(LcsaKvRing), ctypes.c_int32, _P,
                                     ctypes.POINTER(LcsaRope), ctypes.POINTER(LcsaTensor),
@@ -476,6 +481,52 @@ def attend_ring(plan: Plan, q, k_ring, v_ring, ring: LcsaKvRing, row_ptr, col_id
                                ctypes.byref(ov), lse.data_ptr() if lse is not None else None,
                                ws_ptr, ws_bytes, _stream_ptr(q, stream))
     _check(st, "lcsa_attend_ring")
+    if return_lse:
+        return out, lse
+    return out
+
+
+def attend_varlen(plan: Plan, q, k, v, row_ptr, col_idx, out=None, return_lse: bool = False,
+                  workspace=None, ring: LcsaKvRing = None, stream=None):
+    """lcsa_attend_varlen: attention over a CSR whose rows differ in length
+    (a threshold selection), rows taken longest first.  k, v are the
+    contiguous KV window, or the rings when `ring` is given.  Same result as
+    attend / attend_ring to rounding."""
+    import torch
+    _check_shape(q, plan, "q_tokens", "q")
+    if ring is None:
+        _check_shape(k, plan, "kv_tokens", "k")
+        _check_shape(v, plan, "kv_tokens", "v")
+    else:
+        _check_ring_tensor(k, plan, ring.slots, "k_ring")
+        _check_ring_tensor(v, plan, ring.slots, "v_ring")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != plan.info["rows"] + 1 or not row_ptr.is_contiguous():
+        raise ValueError("row_ptr must hold rows + 1 contiguous int32")
+    if not col_idx.is_contiguous():
+        raise ValueError("col_idx must be contiguous")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    else:
+        _check_shape(out, plan, "q_tokens", "out")
+    lse = None
+    if return_lse:
+        d = plan.desc
+        lse = torch.empty((d["batch"], d["heads"], plan.info["q_tokens"]), dtype=torch.float32,
+                          device=q.device)
+    if workspace is None:
+        workspace = torch.empty(int(plan.info["attend_workspace_bytes"]), dtype=torch.uint8,
+                                device=q.device)
+    qv, kv, vv, ov = tensor_view(q), tensor_view(k), tensor_view(v), tensor_view(out)
+    st = _lib.lcsa_attend_varlen(plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
+                                 ctypes.byref(ring) if ring is not None else None,
+                                 row_ptr.data_ptr(),
+                                 col_idx.data_ptr() if col_idx.numel() else None, col_idx.numel(),
+                                 ctypes.byref(ov), lse.data_ptr() if lse is not None else None,
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream_ptr(q, stream))
+    _check(st, "lcsa_attend_varlen")
     if return_lse:
         return out, lse
     return out

@@ -183,20 +183,28 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   // order (workgroup ids go round-robin over the XCDs; XCD x gets the
   // contiguous range [start_x, start_x + count_x) of the visiting order);
   // later workgroups take piece `piece` of a split row.
+  // With a row order, workgroup i takes row order[i]: the order is meant to
+  // be dispatched as it stands (longest rows first), round-robin over the
+  // XCDs.
   int64_t row, item = -1;
   int piece = -1;
   {
     const int64_t pid = blockIdx.x, n = p.full_rows;
     if (pid < n) {
-      const int64_t xcd = pid % kXcds, idx = pid / kXcds;
-      const int64_t per = n / kXcds, rem = n % kXcds;
-      row = xcd * per + (xcd < rem ? xcd : rem) + idx;
+      if (p.order) {
+        row = pid;
+      } else {
+        const int64_t xcd = pid % kXcds, idx = pid / kXcds;
+        const int64_t per = n / kXcds, rem = n % kXcds;
+        row = xcd * per + (xcd < rem ? xcd : rem) + idx;
+      }
     } else {
       item = pid - n;
       row = n + item / p.pieces;
       piece = (int)(item % p.pieces);
     }
-    row = visit_row(g, p.tile, row);
+    row = p.order ? (int64_t)((const __attribute__((address_space(4))) int32_t*)p.order)[row]
+                  : visit_row(g, p.tile, row);
   }
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;
@@ -537,7 +545,7 @@ template <int BT>
 __global__ void __launch_bounds__(kMergeThreads) attend_merge_kernel(AttendParams p) {
   const GridGeom& g = p.g;
   const int64_t tr = blockIdx.x;
-  const int64_t row = visit_row(g, p.tile, p.full_rows + tr);
+  const int64_t row = p.order ? (int64_t)p.order[p.full_rows + tr] : visit_row(g, p.tile, p.full_rows + tr);
   const int t = threadIdx.x, qi = (int)blockIdx.y * 16 + (t >> 4), c0 = (t & 15) * 8;
   const int qb = (int)(row % g.nqb);
   const int64_t bh = row / g.nqb;
@@ -614,6 +622,113 @@ __global__ void __launch_bounds__(kMergeThreads) attend_merge_kernel(AttendParam
   }
 }
 
+// Longest-first row order for CSRs whose rows differ in length (threshold
+// selections, caller masks).  Workgroups take rows in dispatch order, so with
+// rows in the visiting order a long row started late sets the finish time;
+// longest first, the short rows fill in at the end and the rows of the last,
+// partly filled round, which are split, are the shortest.
+
+// len[r]: row r's CSR range after the entries outside [0, nkb) at its end are
+// cut off, as the attention kernel cuts them (one wave per row).
+__global__ void __launch_bounds__(256) row_len_kernel(const int32_t* row_ptr, const int32_t* col_idx,
+                                                      int64_t nnz, int64_t rows, int nkb,
+                                                      int32_t* len) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int n = (int)nnz;
+  int start = row_ptr[r], end = row_ptr[r + 1];
+  start = start < 0 ? 0 : (start > n ? n : start);
+  end = end < start ? start : (end > n ? n : end);
+  int e = end, cut = start;
+  while (e > start) {
+    const int i = e - 64 + lane;
+    const int kb = i >= start ? col_idx[i] : -1;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(kb >= 0 && kb < nkb);
+    if (m) {
+      cut = e - 64 + (64 - __clzll(m));
+      break;
+    }
+    e -= 64;
+  }
+  if (lane == 0) len[r] = cut - start;
+}
+
+// order: the rows by descending length (lengths of kOrderBuckets - 1 and up
+// share the first bucket), rows of equal length in the visiting order (which
+// keeps neighbouring positions together for the L2 caches).  One workgroup:
+// each wave counts the lengths of its contiguous share of the visiting order,
+// the counts give every (bucket, wave) its first position, and each wave
+// then places its rows, 64 at a time, ranking lanes of equal length by lane.
+// Stable, so the order is the same on every run.
+constexpr int kOrderBuckets = 512;
+constexpr int kOrderWaves = 16;
+__global__ void __launch_bounds__(kOrderWaves * 64) row_order_kernel(GridGeom g, int tile,
+                                                                     int64_t rows,
+                                                                     const int32_t* len,
+                                                                     int32_t* order) {
+  __shared__ int32_t base[kOrderWaves][kOrderBuckets];
+  __shared__ int32_t total[2][kOrderBuckets];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kOrderWaves * kOrderBuckets; i += kOrderWaves * 64) (&base[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t per = (rows + kOrderWaves - 1) / kOrderWaves;
+  const int64_t e0 = min(rows, wave * per), e1 = min(rows, e0 + per);
+  auto bucket = [&](int64_t row) {
+    const int l = len[row];
+    return kOrderBuckets - 1 - (l < 0 ? 0 : (l > kOrderBuckets - 1 ? kOrderBuckets - 1 : l));
+  };
+  for (int64_t e = e0 + lane; e < e1; e += 64) atomicAdd(&base[wave][bucket(visit_row(g, tile, e))], 1);
+  __syncthreads();
+  // exclusive prefix of the bucket totals (bucket 0 = longest; a scan in
+  // log2(buckets) steps), then of the waves within each bucket
+  static_assert(kOrderBuckets <= kOrderWaves * 64, "one thread per bucket");
+  int own = 0;
+  if (tid < kOrderBuckets) {
+    for (int w = 0; w < kOrderWaves; ++w) own += base[w][tid];
+    total[0][tid] = own;
+  }
+  __syncthreads();
+  int src = 0;
+  for (int d = 1; d < kOrderBuckets; d <<= 1) {
+    if (tid < kOrderBuckets)
+      total[src ^ 1][tid] = total[src][tid] + (tid >= d ? total[src][tid - d] : 0);
+    src ^= 1;
+    __syncthreads();
+  }
+  if (tid < kOrderBuckets) {
+    int s = total[src][tid] - own;
+    for (int w = 0; w < kOrderWaves; ++w) {
+      const int c = base[w][tid];
+      base[w][tid] = s;
+      s += c;
+    }
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t c0 = e0; c0 < e1; c0 += 64) {
+    const int64_t e = c0 + lane;
+    const bool ok = e < e1;
+    const int64_t row = ok ? visit_row(g, tile, e) : 0;
+    const int b = ok ? bucket(row) : -1;
+    int rank = 0, cnt = 0;
+    uint64_t todo = __builtin_amdgcn_ballot_w64(ok);
+    while (todo) {
+      const int bl = __builtin_amdgcn_readlane(b, __builtin_ctzll(todo));
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok && b == bl);
+      if (ok && b == bl) {
+        rank = __popcll(m & below);
+        cnt = __popcll(m);
+      }
+      todo &= ~m;
+    }
+    if (ok) order[base[wave][b] + rank] = (int32_t)row;
+    // every lane has read its base above (a wave's LDS operations complete
+    // in order); the first lane of each length moves it on
+    if (ok && rank == 0) base[wave][b] += cnt;
+  }
+}
+
 template <int BT>
 hipError_t launch_bt(const AttendParams& p, hipStream_t stream) {
   const int64_t split = p.rows - p.full_rows;
@@ -632,6 +747,18 @@ hipError_t launch_bt(const AttendParams& p, hipStream_t stream) {
 hipError_t launch_attend(const AttendParams& p, int block_tokens, hipStream_t stream) {
   if (p.rows <= 0) return hipSuccess;
   return block_tokens == 128 ? launch_bt<128>(p, stream) : launch_bt<64>(p, stream);
+}
+
+hipError_t launch_row_order(const AttendParams& p, int32_t* len, int32_t* order,
+                            hipStream_t stream) {
+  if (p.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_len_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream,
+                     p.row_ptr, p.col_idx, p.nnz, p.rows, p.g.nkb, len);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_order_kernel, dim3(1), dim3(kOrderWaves * 64), 0, stream, p.g, p.tile,
+                     p.rows, static_cast<const int32_t*>(len), order);
+  return hipGetLastError();
 }
 
 }  // namespace lcsa

@@ -238,12 +238,13 @@ lcsa_status select_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   return LCSA_OK;
 }
 
-// Shared body of lcsa_attend (ring == NULL) and lcsa_attend_ring.
+// Shared body of lcsa_attend (ring == NULL), lcsa_attend_ring and, with
+// varlen, lcsa_attend_varlen (rows longest first).
 lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tensor* q,
                         const lcsa_tensor* k, const lcsa_tensor* v, const lcsa_kv_ring* ring,
                         const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
                         const lcsa_tensor* o, float* d_lse, void* d_workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool varlen = false) {
   if (!plan) return fail(LCSA_ERR_NULL, "%s: plan is NULL", fn);
   const lcsa_plan_info& in = plan->info;
   lcsa_status st;
@@ -265,6 +266,10 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
     return fail(LCSA_ERR_SHAPE, "%s: token stride too large for one key block", fn);
   if (d_workspace && reinterpret_cast<uintptr_t>(d_workspace) % 256)
     return fail(LCSA_ERR_ALIGN, "%s: workspace not 256-byte aligned", fn);
+  if (varlen && (!d_workspace || workspace_bytes < in.attend_workspace_bytes))
+    return fail(LCSA_ERR_WORKSPACE, "%s needs a workspace of %llu bytes, got %llu", fn,
+                (unsigned long long)in.attend_workspace_bytes,
+                (unsigned long long)(d_workspace ? workspace_bytes : 0));
   if ((st = check_device())) return st;
 
   // Split the rows of a last, partly filled round of workgroups: with S
@@ -314,7 +319,17 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   ap.tile = attend_tile(slots, plan->desc.q_frames, in.nbh, in.nbw);
   ap.part = static_cast<float*>(d_workspace);
   ap.scale_log2 = static_cast<float>(in.scale * 1.4426950408889634);
-  const hipError_t e = launch_attend(ap, in.block_tokens, static_cast<hipStream_t>(stream));
+  ap.order = nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (varlen) {
+    int32_t* len = reinterpret_cast<int32_t*>(static_cast<char*>(d_workspace) +
+                                              attend_pieces_bytes(in.block_tokens));
+    int32_t* order = len + in.rows;
+    const hipError_t e = launch_row_order(ap, len, order, s);
+    if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "row order launch: %s", hipGetErrorString(e));
+    ap.order = order;
+  }
+  const hipError_t e = launch_attend(ap, in.block_tokens, s);
   if (e != hipSuccess) return fail(LCSA_ERR_LAUNCH, "attend launch: %s", hipGetErrorString(e));
   return LCSA_OK;
 }
@@ -495,6 +510,16 @@ lcsa_status lcsa_attend(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tenso
   lcsa::clear_error();
   return lcsa::attend_impl("lcsa_attend", plan, q, k, v, nullptr, d_row_ptr, d_col_idx, nnz, o,
                            d_lse, d_workspace, workspace_bytes, stream);
+}
+
+lcsa_status lcsa_attend_varlen(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                               const lcsa_tensor* v, const lcsa_kv_ring* ring,
+                               const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
+                               const lcsa_tensor* o, float* d_lse, void* d_workspace,
+                               size_t workspace_bytes, void* stream) {
+  lcsa::clear_error();
+  return lcsa::attend_impl("lcsa_attend_varlen", plan, q, k, v, ring, d_row_ptr, d_col_idx, nnz,
+                           o, d_lse, d_workspace, workspace_bytes, stream, true);
 }
 
 lcsa_status lcsa_attend_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k_ring,

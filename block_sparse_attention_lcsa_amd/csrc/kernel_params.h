@@ -97,6 +97,10 @@ struct AttendParams {
   int32_t tile;
   float* part;           // [items][BT][128] partial O, then [items][BT][2] (m, l)
   float scale_log2;      // softmax scale * log2(e)
+  // Optional order of the rows (a permutation of [0, rows)): workgroup i
+  // takes row order[i] instead of the visiting order above (the split rows
+  // are order[full_rows ..]).  NULL: the visiting order.
+  const int32_t* order;
 };
 
 }  // namespace lcsa

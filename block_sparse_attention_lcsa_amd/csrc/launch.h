@@ -14,6 +14,10 @@ hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, bool ro
                        hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, int batch, int max_window, hipStream_t stream);
 hipError_t launch_attend(const AttendParams& p, int block_tokens, hipStream_t stream);
+// Longest-first order of the CSR rows of p (p.row_ptr, p.col_idx, p.nnz,
+// p.rows, p.g, p.tile) into order[rows], with len[rows] as scratch.
+hipError_t launch_row_order(const AttendParams& p, int32_t* len, int32_t* order,
+                            hipStream_t stream);
 
 // Bytes of one split piece's partial result (O in float32, then m and l).
 inline int64_t attend_piece_bytes(int block_tokens) {

@@ -24,6 +24,13 @@ constexpr int kHeadDim = 128;
 // Compute units of the largest gfx950 device (MI355X, MI350X); sizes the
 // attention workspace for split rows.
 constexpr uint64_t kMaxCus = 256;
+// Bytes of the attention workspace's split-piece area: one device-wide round
+// of pieces (8 waves per CU) of BT x (128 + 2) float32 each.  The row lengths
+// and row order of lcsa_attend_varlen follow it.
+inline uint64_t attend_pieces_bytes(int block_tokens) {
+  const uint64_t bt = static_cast<uint64_t>(block_tokens);
+  return kMaxCus * (8 / (bt / 32)) * bt * (128 + 2) * 4;
+}
 
 // Record a formatted error for lcsa_last_error() and return the status.
 lcsa_status fail(lcsa_status st, const char* fmt, ...);

@@ -204,9 +204,11 @@ lcsa_status lcsa_plan_create(const lcsa_desc* d, lcsa_plan_t* out) {
                                   static_cast<uint64_t>(nqb) * 8ull +
                               static_cast<uint64_t>(in.kv_frames) * in.kcache_slot_bytes;
   // Attend: at most one partly filled round of split pieces, i.e. as many
-  // pieces as workgroups fit on the largest gfx950 device at once.
+  // pieces as workgroups fit on the largest gfx950 device at once; then, for
+  // lcsa_attend_varlen, the row lengths and row order (int32 [rows] each).
   const uint64_t bt = static_cast<uint64_t>(in.block_tokens);
-  in.attend_workspace_bytes = lcsa::kMaxCus * (8 / (bt / 32)) * bt * (128 + 2) * 4;
+  in.attend_workspace_bytes = lcsa::attend_pieces_bytes(static_cast<int>(bt)) +
+                              (static_cast<uint64_t>(rows) * 8 + 255) / 256 * 256;
 
   try {
     p->row_ptr.resize(static_cast<size_t>(rows) + 1);

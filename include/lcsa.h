@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LCSA_ABI_VERSION 6
+#define LCSA_ABI_VERSION 7
 
 typedef int32_t lcsa_status;
 #define LCSA_OK 0
@@ -405,6 +405,30 @@ lcsa_status lcsa_attend_ring(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_
                              const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
                              const lcsa_tensor* o, float* d_lse, void* d_workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention for a CSR whose rows differ in length, such as the
+ * output of lcsa_select_reuse (rows keep every block at or above a stored
+ * threshold, so their lengths vary: the steady threshold reuse of the
+ * FlashVSR Hopper PR page, "Remove the remaining control-plane tax"), or a
+ * caller's mask.  Same result as lcsa_attend (ring == NULL) or
+ * lcsa_attend_ring (ring given), to rounding: rows are taken longest first
+ * instead of in the plan's visiting order, so that no long row starts last
+ * and the rows split in the last, partly filled round are the shortest.  The
+ * order is computed on the device from d_row_ptr / d_col_idx (two small
+ * kernels before the attention kernel; stable, so every run takes the same
+ * order and gives the same bits).
+ *  k, v            the contiguous KV window (ring == NULL) or the rings.
+ *  d_workspace     required, 256-byte aligned, at least
+ *                  attend_workspace_bytes: the split pieces as in
+ *                  lcsa_attend, then the row lengths and the row order.
+ *  Other arguments as lcsa_attend.
+ * Errors: as lcsa_attend (WORKSPACE for a NULL or short workspace), plus
+ * INVALID (ring out of range). */
+lcsa_status lcsa_attend_varlen(lcsa_plan_t plan, const lcsa_tensor* q, const lcsa_tensor* k,
+                               const lcsa_tensor* v, const lcsa_kv_ring* ring,
+                               const int32_t* d_row_ptr, const int32_t* d_col_idx, int64_t nnz,
+                               const lcsa_tensor* o, float* d_lse, void* d_workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* lcsa_status_string(lcsa_status status);

@@ -321,3 +321,94 @@ def test_ring_rope_steady_matches_ring_rope_select():
     rows = _check_padded(g, rq.cpu().numpy(), cq.cpu().numpy(), plan.info["max_window"])
     say(f"  ring + rope: steady equals ring rotary select; reuse kept {sum(len(r) for r in rows)} "
         f"blocks against {int(rp1[-1])} top-k")
+
+
+@pytest.mark.parametrize("name", SMALL + ["stream_768x1280"])
+def test_attend_varlen(name):
+    """lcsa_attend_varlen on a reused-threshold CSR (rows of many lengths,
+    some empty): every row written (the output starts as NaN), the same bits
+    on a second run, the oracle's attention on the small grids, and the
+    whole-row attention's result to rounding: bit for bit on every row that
+    is not split (at most rows % workgroup slots rows are)."""
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    _, inp1 = host_inputs(name, seed=1)
+    _, _, s1 = oracle.select(g, li.bf16_bits_to_f64(inp1.q), li.bf16_bits_to_f64(inp1.k))
+    tau = oracle.row_thresholds(g, s1)
+    tau[::7] = np.inf
+    rp, ci = lcsa.select_reuse(plan, q, k, torch.from_numpy(tau).cuda())
+    lens = (ci.view(-1, plan.info["max_window"]) >= 0).sum(dim=1)
+    say(f"  {name}: row lengths {int(lens.min())}..{int(lens.max())}, "
+        f"{int((lens == 0).sum())} empty rows")
+    runs = []
+    for _ in range(2):
+        out = torch.full_like(q, float("nan"))
+        o, lse = lcsa.attend_varlen(plan, q, k, v, rp, ci, out=out, return_lse=True)
+        torch.cuda.synchronize()
+        assert not bool(torch.isnan(o.float()).any()), "a row was not written"
+        runs.append((o, lse))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+    o_v, lse_v = runs[0]
+    o_w, lse_w = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True, split_tail=False)
+    torch.cuda.synchronize()
+    d = float((o_v.float() - o_w.float()).abs().max())
+    fin = torch.isfinite(lse_w)
+    assert torch.equal(fin, torch.isfinite(lse_v))
+    dl = float((lse_v[fin] - lse_w[fin]).abs().max()) if bool(fin.any()) else 0.0
+    assert d <= 1e-2 and dl <= 2e-3
+    rows, bt = plan.info["rows"], plan.info["block_tokens"]
+    props = torch.cuda.get_device_properties(0)
+    slots = props.multi_processor_count * (8 // (bt // 32))
+    # rows whose output differs at all from the whole-row run
+    pd = plan.desc
+    ov = o_v.view(pd["batch"], -1, pd["heads"], 128)
+    ow = o_w.view(pd["batch"], -1, pd["heads"], 128)
+    differ = 0
+    for r, b, h, qb in _rows(g):
+        tok = oracle.block_tokens(g, qb)
+        differ += int(not torch.equal(ov[b, tok, h], ow[b, tok, h]))
+    say(f"  {name}: vs whole rows O max|d| {d:.3e}, LSE max|d| {dl:.3e}; "
+        f"{differ} of {rows} rows differ (at most {rows % slots} split)")
+    assert differ <= rows % slots
+    if name in SMALL:
+        _, inp = host_inputs(name)
+        o_ref, lse_ref = oracle.attend(g, li.bf16_bits_to_f32(inp.q), li.bf16_bits_to_f32(inp.k),
+                                       li.bf16_bits_to_f32(inp.v), rp.cpu().numpy().astype(np.int64),
+                                       ci.cpu().numpy().astype(np.int64))
+        compare_output(bf16_to_np(o_v), o_ref, f"{name} varlen vs oracle")
+        lse_h = lse_v.cpu().numpy()
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isneginf(lse_h), np.isneginf(lse_ref))
+        assert float(np.abs(lse_h[fin] - lse_ref[fin]).max(initial=0.0)) <= 2e-3
+
+
+def test_attend_varlen_ring_and_top_k():
+    """The ring form of lcsa_attend_varlen gives the contiguous form's bits;
+    on a top-k CSR (equal rows) it gives attend's result to rounding."""
+    name = "small_edges"
+    desc, q, k, v = device_qkv(name)
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    _, inp1 = host_inputs(name, seed=1)
+    _, _, s1 = oracle.select(g, li.bf16_bits_to_f64(inp1.q), li.bf16_bits_to_f64(inp1.k))
+    rp, ci = lcsa.select_reuse(plan, q, k, torch.from_numpy(oracle.row_thresholds(g, s1)).cuda())
+    kvf = plan.info["kv_frames"]
+    ft = desc["grid_h"] * desc["grid_w"]
+    slots = kvf + 2
+    fs = [int(x) for x in np.random.default_rng(11).permutation(slots)[:kvf]]
+    ring = lcsa.kv_ring(slots, fs)
+    kr = torch.zeros((desc["batch"], slots * ft, desc["heads"], 128), dtype=q.dtype, device="cuda")
+    vr = torch.zeros_like(kr)
+    for t in range(kvf):
+        kr[:, fs[t] * ft:(fs[t] + 1) * ft] = k[:, t * ft:(t + 1) * ft]
+        vr[:, fs[t] * ft:(fs[t] + 1) * ft] = v[:, t * ft:(t + 1) * ft]
+    o_c = lcsa.attend_varlen(plan, q, k, v, rp, ci)
+    o_r = lcsa.attend_varlen(plan, q, kr, vr, rp, ci, ring=ring)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_r)
+    rp_t, ci_t = lcsa.select(plan, q, k)
+    o_t = lcsa.attend(plan, q, k, v, rp_t, ci_t)
+    o_tv = lcsa.attend_varlen(plan, q, k, v, rp_t, ci_t)
+    torch.cuda.synchronize()
+    assert float((o_t.float() - o_tv.float()).abs().max()) <= 1e-2

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert lcsa.abi_version() == 6
+    assert lcsa.abi_version() == 7
     lib = ctypes.CDLL(lcsa.lib_path())
     lib.lcsa_status_string.restype = ctypes.c_char_p
     texts = {lib.lcsa_status_string(i).decode() for i in range(9)}
@@ -72,9 +72,11 @@ def test_plan_matches_oracle_geometry(name):
     assert inf["rows"] == len(rp) - 1 and inf["nnz"] == rp[-1]
     assert np.array_equal(p.row_ptr(), rp)
     assert inf["useful_flops"] == oracle.useful_flops(g, rp)
-    # room for one device-wide round of split pieces: 256 CUs x 8 waves
     bt = g.block_tokens
-    assert inf["attend_workspace_bytes"] == 256 * (8 // (bt // 32)) * bt * (128 + 2) * 4
+    # one device-wide round of split pieces (256 CUs x 8 waves), then the
+    # row lengths and row order of lcsa_attend_varlen
+    assert inf["attend_workspace_bytes"] == (256 * (8 // (bt // 32)) * bt * (128 + 2) * 4
+                                             + -(-8 * inf["rows"] // 256) * 256)
     # pooled K per frame slot, positions in groups of 8 (the last padded)
     assert inf["kcache_slot_bytes"] == g.batch * g.heads * 128 * (-(-g.nbf // 8) * 8) * 8
     assert inf["select_workspace_bytes"] == (g.batch * g.heads * 128 * g.nqb * 8
@@ -357,3 +359,33 @@ def test_noalloc_select_statuses():
         good = _fake_view()
         assert lib.lcsa_select_noalloc(_TINY.handle, ctypes.byref(good), ctypes.byref(good),
                                        0x20000, 0x30000, None, None) == 6    # DEVICE
+
+
+def test_attend_varlen_validation_statuses():
+    """lcsa_attend_varlen needs its workspace (the split pieces, then the row
+    lengths and order): NULL or short is LCSA_ERR_WORKSPACE, checked on the
+    host with the other arguments before any HIP call; a ring out of range is
+    INVALID as for lcsa_attend_ring."""
+    p = lcsa.Plan.from_desc(li.CONFIGS["small_edges"])      # kv_frames 3
+    q, kv = _fake_view(plan=p), _fake_view(plan=p, tokens="kv")
+    need = p.info["attend_workspace_bytes"]
+    lib = lcsa._lib
+
+    def varlen(k=kv, v=kv, ring=None, ws=0x40000, ws_bytes=need, nnz=8):
+        return lib.lcsa_attend_varlen(p.handle, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                      ctypes.byref(ring) if ring is not None else None,
+                                      0x20000, 0x30000, nnz, ctypes.byref(q), None, ws, ws_bytes,
+                                      None)
+    assert varlen(ws=None, ws_bytes=0) == 5                           # WORKSPACE: NULL
+    assert varlen(ws_bytes=need - 1) == 5                             # WORKSPACE: short
+    assert varlen(ws=0x40040) == 4                                    # ALIGN workspace
+    assert varlen(nnz=-1) == 2                                        # INVALID nnz
+    assert varlen(v=q) == 3                                           # SHAPE: v extents
+    ft = p.desc["grid_h"] * p.desc["grid_w"]
+    ring4 = _fake_view(plan=p, tokens=4 * ft)
+    assert varlen(k=ring4, v=ring4, ring=lcsa.kv_ring(4, [3, 0, 4])) == 2   # INVALID slot
+    assert lib.lcsa_attend_varlen(None, None, None, None, None, None, None, 0, None, None, None,
+                                  0, None) == 1                        # NULL plan
+    if not torch.cuda.is_available():
+        assert varlen() == 6                                          # DEVICE on CPU hosts
+        assert varlen(k=ring4, v=ring4, ring=lcsa.kv_ring(4, [3, 0, 1])) == 6
