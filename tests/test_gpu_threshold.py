@@ -233,9 +233,11 @@ def test_ring_and_rope_forms_match():
     assert torch.equal(rq3, rq4) and torch.equal(cq3, cq4)
 
 
-def test_threshold_chain_in_graph():
+@pytest.mark.parametrize("varlen", [False, True])
+def test_threshold_chain_in_graph(varlen):
     """Steady select on one chunk, reuse on the next and attention on the
-    padded CSR, captured once in a HIP graph and replayed on new inputs:
+    padded CSR (lcsa_attend, or lcsa_attend_varlen with its row-order
+    kernels), captured once in a HIP graph and replayed on new inputs:
     bitwise equal to eager calls every time."""
     name = "small_edges"
     desc, _, _, _ = device_qkv(name)
@@ -252,7 +254,10 @@ def test_threshold_chain_in_graph():
     def chain():
         _, _, kth = lcsa.select_steady(plan, qa, ka, workspace=sel_ws)
         rp, ci = lcsa.select_reuse(plan, qb, kb, kth, workspace=sel_ws)
-        lcsa.attend(plan, qb, kb, vb, rp, ci, out=out, workspace=att_ws)
+        if varlen:
+            lcsa.attend_varlen(plan, qb, kb, vb, rp, ci, out=out, workspace=att_ws)
+        else:
+            lcsa.attend(plan, qb, kb, vb, rp, ci, out=out, workspace=att_ws)
         return kth, rp, ci
 
     def load(seed):

@@ -15,6 +15,9 @@ two sides' float64 scores tie exactly too:
              among them;
   const_k    every key token is the same vector: every row's window ties.
 
+wide_726 has windows of 216..726 candidates (12 per lane), the 4K chunk's
+top-k width.
+
 The CSR must equal the oracle's exactly (no near-tie allowance: these ties
 are exact on both sides), for lcsa_select and lcsa_select_steady, and no
 entry of row_ptr or col_idx past its end may be written (both buffers carry
@@ -35,7 +38,12 @@ pytestmark = pytest.mark.gpu
 import block_sparse_attention_lcsa_amd as lcsa  # noqa: E402  (fails loudly if not built)
 
 WORKLOADS = ["tiny", "tiny_window", "small_edges", "small_16x8", "stream_768x1280",
-             "first_768x1280"]
+             "first_768x1280", "wide_726"]
+# A window of up to 726 candidates (12 per lane) with k = 45: the widest
+# top-k width of the 4K chunk, with ties.
+EXTRA = {"wide_726": dict(batch=1, heads=2, head_dim=128, grid_h=88, grid_w=88, q_frames=4,
+                          cached_frames=2, kv_ratio=1.5, block_t=1, block_h=8, block_w=8,
+                          local_range=11, topk_ratio=0.0, topk=45, scale=0.0)}
 MODES = ["zero_q", "dup_k", "const_k"]
 GUARD = 4096
 SENTINEL = 0x5A5A5A5A
@@ -52,7 +60,7 @@ def _announce(request):
 
 
 def _tied_inputs(name, mode):
-    desc = dict(li.CONFIGS[name])
+    desc = dict(EXTRA[name] if name in EXTRA else li.CONFIGS[name])
     inp = li.generate(desc, seed=7)
     g = oracle.geometry(desc)
     q, k = inp.q.copy(), inp.k.copy()
