@@ -282,21 +282,24 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   }
   const char* kbase = reinterpret_cast<const char*>(p.k.data + (int64_t)b * p.k.sb + (int64_t)h * p.k.sh);
   const char* vbase = reinterpret_cast<const char*>(p.v.data + (int64_t)b * p.v.sb + (int64_t)h * p.v.sh);
-  auto block_offset = [&](int kb, int64_t ss2) {
+  auto block_tok0 = [&](int kb) {
     const int t = fast_div(kb, g.nbf_m, g.nbf_s), ps = kb - t * g.nbf;
     const int kby = fast_div(ps, g.nbw_m, g.nbw_s), kbx = ps - kby * g.nbw;
-    const int64_t tok0 = ((int64_t)g.kv_slot[t] * g.grid_h + (int64_t)kby * g.block_h) * g.grid_w +
-                         (int64_t)kbx * g.block_w;
-    return tok0 * ss2;
+    return ((int64_t)g.kv_slot[t] * g.grid_h + (int64_t)kby * g.block_h) * g.grid_w +
+           (int64_t)kbx * g.block_w;
   };
   const uint32_t k_lds_addr = lds_address(k_lds) + wave * 1024;
   const uint32_t v_lds_addr = lds_address(v_lds) + wave * 1024;
   // Next CSR position >= i holding a valid key block (uniform; scalar loads).
-  auto next_valid = [&](int i) {
+  auto next_valid = [&](int i, int& kbv) {
     i = __builtin_amdgcn_readfirstlane(i);
+    kbv = 0;
     while (i < end) {
       const int kb = col_idx[i];
-      if (kb >= 0 && kb < g.nkb) break;
+      if (kb >= 0 && kb < g.nkb) {
+        kbv = kb;
+        break;
+      }
       i = __builtin_amdgcn_readfirstlane(i + 1);
     }
     return i;
@@ -324,23 +327,32 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   float m_run = -__builtin_huge_valf(), l_run = 0.0f;
   const float sl2 = p.scale_log2;
 
-  int it = next_valid(start);
+  int kb_cur;
+  int it = next_valid(start, kb_cur);
   const int first = it;
+  int64_t tok_cur = 0;
   if (it < end) {   // K of the first block
-    const char* src = kbase + block_offset(col_idx[it], row_stride_k);
+    tok_cur = block_tok0(kb_cur);
+    const char* src = kbase + tok_cur * row_stride_k;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma16(src, koff[i], k_lds_addr + i * T::kWaves * 1024);
   }
 
   while (it < end) {
-    const int kb = col_idx[it];
     // V(it) is issued one load per S step below, so the loads do not queue
-    // up in front of the MFMAs.  Its source address (a scalar load of the
-    // frame slot plus scalar arithmetic) is settled here, before the waits:
-    // left to the compiler it lands after the barrier, where the wait for
-    // that scalar load would also wait for the first K operand reads.
-    const char* vsrc = vbase + block_offset(kb, row_stride_v);
-    asm volatile("" : "+s"(vsrc));
+    // up in front of the MFMAs.  The next valid block and its first token
+    // (two scalar round trips: the CSR entry, then the frame slot) are
+    // settled here, before the waits, where the wave waits for K(it) anyway;
+    // left to the compiler they land in front of the softmax.
+    const char* vsrc = vbase + tok_cur * row_stride_v;
+    int kb_nx;
+    const int nx = next_valid(it + 1, kb_nx);
+    const int64_t tok_nx = nx < end ? block_tok0(kb_nx) : tok_cur;
+    // K(nx) is issued one load per PV step below (after the V barrier, when
+    // every wave is done with K(it)); on the last block the current block is
+    // re-read instead, which keeps the loop body branch-free.
+    const char* ksrc = kbase + tok_nx * row_stride_k;
+    asm volatile("" : "+s"(vsrc), "+s"(ksrc));
     wait_vmcnt<0>();          // K(it) landed (this wave's share)
     barrier_raw();            // ... everyone's; V buffer free (PV of it-1 done)
 
@@ -375,12 +387,6 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int nx = next_valid(it + 1);
-    // K(nx) is issued one load per PV step below (after the V barrier, when
-    // every wave is done with K(it)); on the last block the current block is
-    // re-read instead, which keeps the loop body branch-free.
-    const char* ksrc = kbase + block_offset(col_idx[nx < end ? nx : it], row_stride_k);
-    asm volatile("" : "+s"(ksrc));   // settled now, not after the PV operand reads
 
     // Wave priorities: softmax 2, PV 1, S 0.  The two waves sharing a SIMD
     // come from different workgroups and tend to fall into step (the one
@@ -489,6 +495,7 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
     }
     __builtin_amdgcn_s_setprio(0);
     it = nx;
+    tok_cur = tok_nx;
   }
   wait_vmcnt<0>();            // no load may still target LDS when the workgroup retires
 
