@@ -24,6 +24,9 @@ constexpr int kHeadDim = 128;
 // Compute units of the largest gfx950 device (MI355X, MI350X); sizes the
 // attention workspace for split rows.
 constexpr uint64_t kMaxCus = 256;
+// Memory-side cache (Infinity Cache) of an MI355X: data a pass streams once
+// that is larger than this cannot stay there for the next kernel anyway.
+constexpr uint64_t kMemorySideCacheBytes = 256ull << 20;
 // Bytes of the attention workspace's split-piece area: one device-wide round
 // of pieces (8 waves per CU) of BT x (128 + 2) float32 each.  The row lengths
 // and row order of lcsa_attend_varlen follow it.

@@ -54,6 +54,22 @@ constexpr int kMaxPerLane = kMaxWindow / 64;   // window candidates per lane
 __device__ inline double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ inline double bf16_hi(uint32_t w) { return (double)__uint_as_float(w & 0xffff0000u); }
 
+// 16-byte load of Q or K in the pooling pass.  STREAM marks it non-temporal:
+// when Q and K are far larger than the caches, the stream then no longer
+// evicts the pass's own dirty output lines from L2 while it runs.  When they
+// fit in the memory-side cache, plain loads leave them there for the
+// attention that follows.
+template <bool STREAM>
+__device__ inline uint4 load16_qk(const uint16_t* ptr) {
+  if constexpr (STREAM) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(ptr);
+  }
+}
+
 // Raster token index of element j (0 .. block_tokens-1) of block (t, by, bx).
 __device__ inline int64_t block_token(const GridGeom& g, int t, int by, int bx, int j) {
   const int y = by * g.block_h + (j >> g.log2_bw);
@@ -87,7 +103,8 @@ __device__ inline uint32_t rope_pair(uint32_t w, float2 cs) {
 // channels 8c..8c+7 of tokens tg, tg+16, ...  With ROPE each 16-byte slice
 // (channel pairs 4c..4c+3) is first turned by the rotary tables, written to
 // the rotated Q / K output, and the rotated bf16 values are what is pooled.
-template <int BT, bool ROPE>
+// STREAM: non-temporal Q/K loads (see load16_qk).
+template <int BT, bool ROPE, bool STREAM>
 __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
   __shared__ double red[16 * 128];
   const GridGeom& g = p.g;
@@ -143,7 +160,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolParams p) {
   uint4 wv[BT / 16];
 #pragma unroll
   for (int i = 0; i < BT / 16; ++i)
-    wv[i] = *reinterpret_cast<const uint4*>(base + block_token(g, tf, by, bx, tg + 16 * i) * x.ss + c * 8);
+    wv[i] = load16_qk<STREAM>(base + block_token(g, tf, by, bx, tg + 16 * i) * x.ss + c * 8);
   // (cos, sin) of every pair of every token, also loaded up front
   float2 cs[ROPE ? BT / 16 : 1][4];
   if constexpr (ROPE) {
@@ -514,21 +531,33 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   }
 }
 
+template <int BT, bool ROPE>
+void launch_pool_bt(const PoolParams& p, const dim3 grid, bool stream_loads, hipStream_t stream) {
+  if (stream_loads)
+    hipLaunchKernelGGL((pool_kernel<BT, ROPE, true>), grid, dim3(kPoolThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((pool_kernel<BT, ROPE, false>), grid, dim3(kPoolThreads), 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_pool(const PoolParams& p, int batch, int block_tokens, bool rope,
                        hipStream_t stream) {
-  const dim3 grid((p.g.nqb + (p.g.kv_frames - p.k_first) * p.g.nbf) * p.g.heads, 1, batch);
+  const int64_t blocks = p.g.nqb + (int64_t)(p.g.kv_frames - p.k_first) * p.g.nbf;
+  const dim3 grid((unsigned)(blocks * p.g.heads), 1, batch);
+  // Q and K bytes this pass reads against the 256 MiB memory-side cache.
+  const bool stream_loads =
+      (uint64_t)blocks * p.g.heads * batch * block_tokens * 256 > kMemorySideCacheBytes;
   if (block_tokens == 128) {
     if (rope)
-      hipLaunchKernelGGL((pool_kernel<128, true>), grid, dim3(kPoolThreads), 0, stream, p);
+      launch_pool_bt<128, true>(p, grid, stream_loads, stream);
     else
-      hipLaunchKernelGGL((pool_kernel<128, false>), grid, dim3(kPoolThreads), 0, stream, p);
+      launch_pool_bt<128, false>(p, grid, stream_loads, stream);
   } else {
     if (rope)
-      hipLaunchKernelGGL((pool_kernel<64, true>), grid, dim3(kPoolThreads), 0, stream, p);
+      launch_pool_bt<64, true>(p, grid, stream_loads, stream);
     else
-      hipLaunchKernelGGL((pool_kernel<64, false>), grid, dim3(kPoolThreads), 0, stream, p);
+      launch_pool_bt<64, false>(p, grid, stream_loads, stream);
   }
   return hipGetLastError();
 }
