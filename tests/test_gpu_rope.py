@@ -91,6 +91,29 @@ def test_select_rope_matches_oracle(name, pairs):
         compare_output(got, want, f"{name} attend on turned Q, K ({len(rows)} sampled rows)")
 
 
+def test_select_rope_streaming_pass_4k():
+    """At the 184320-token chunk Q and K exceed the memory-side cache, so the
+    pooling pass runs with non-temporal loads (its other form): the turned
+    Q and K must still equal the oracle's bit for bit, and lcsa_select on
+    them must give the rotary select's CSR and scores bitwise."""
+    name = "first_2048x3840"
+    desc, q, k, _ = device_qkv(name)
+    _, inp = host_inputs(name)
+    plan = lcsa.Plan.from_desc(desc)
+    g = oracle.geometry(desc)
+    tab, dtab = _tables(desc)
+    q_rot, k_rot, rp, ci, sc = lcsa.select_rope(plan, q, k, dtab, return_scores=True)
+    rp2, ci2, sc2 = lcsa.select(plan, q_rot, k_rot, return_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp2) and torch.equal(ci, ci2) and torch.equal(sc, sc2)
+    qr = oracle.rope_q(g, li.bf16_bits_to_f64(inp.q), tab)
+    assert np.array_equal(_bits(q_rot), _f64_to_bits(qr)), "turned Q differs from the oracle"
+    del qr
+    kr = oracle.rope_k(g, li.bf16_bits_to_f64(inp.k), tab)
+    assert np.array_equal(_bits(k_rot), _f64_to_bits(kr)), "turned K differs from the oracle"
+    say(f"  {name}: turned Q and K bitwise equal to the oracle; select on them equals the rotary select")
+
+
 def test_select_rope_in_place():
     name = "small_edges"
     desc, q, k, _ = device_qkv(name)
