@@ -607,9 +607,9 @@ def main():
 def time_workloads(names, seed, dev, stream):
     """Step time and select / attend medians of the other named workloads,
     timed with HIP events on the launch stream in this same run: a spin-up
-    of SPIN_UP_S seconds and 10 warm-up steps, then 20 steps back to back (10
+    of SPIN_UP_S seconds and 10 warm-up steps, then 50 steps back to back (20
     at the 184320-token chunk) for the step time, then as many with events
-    around select and attend."""
+    around select and attend (medians, p10 and p90)."""
     import numpy as np
     import torch
     import block_sparse_attention_lcsa_amd as lcsa
@@ -628,7 +628,7 @@ def time_workloads(names, seed, dev, stream):
         ws = torch.empty(max(int(info["select_workspace_bytes"]), 256), dtype=torch.uint8, device=dev)
         att_ws = torch.empty(int(info["attend_workspace_bytes"]), dtype=torch.uint8, device=dev)
         o = torch.empty_like(q)
-        n = 10 if info["q_tokens"] > 100000 else 20
+        n = 20 if info["q_tokens"] > 100000 else 50
 
         def step(ev=None):
             if ev:
@@ -658,9 +658,13 @@ def time_workloads(names, seed, dev, stream):
             step(e)
         torch.cuda.synchronize()
         step_ms = t0.elapsed_time(t1) / n
-        sel = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
-        att = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-        both = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+        sel_t = [e[0].elapsed_time(e[1]) for e in evs]
+        att_t = [e[1].elapsed_time(e[2]) for e in evs]
+        both_t = [e[0].elapsed_time(e[2]) for e in evs]
+        sel, att, both = (float(np.median(x)) for x in (sel_t, att_t, both_t))
+
+        def p10_p90(x):
+            return [float(np.percentile(x, 10)), float(np.percentile(x, 90))]
         flops = float(info["useful_flops"])
         sel_bytes = (2 * desc["batch"] * desc["heads"] * 128 * (info["q_tokens"] + info["kv_tokens"])
                      + 4 * (info["rows"] + 1 + info["nnz"]))
@@ -670,6 +674,8 @@ def time_workloads(names, seed, dev, stream):
             "selected_pairs": info["nnz"], "useful_tflop": flops / 1e12,
             "inputs_sha256": inp.sha256,
             "select_ms_median": sel, "attend_ms_median": att, "select_attend_ms_median": both,
+            "select_ms_p10_p90": p10_p90(sel_t), "attend_ms_p10_p90": p10_p90(att_t),
+            "select_attend_ms_p10_p90": p10_p90(both_t),
             "attend_tflops": flops / (att * 1e-3) / 1e12,
             "attend_frac_of_bf16_peak": flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "select_gbs": sel_bytes / (sel * 1e-3) / 1e9,
