@@ -21,9 +21,11 @@ over worker processes (1 warm-up and 3 timed runs, medians); parity = the
 GPU's CSR, O and LSE of that step against the oracle's, on every row and
 element; workloads = select and attend medians of the other named workloads
 in the same run.  Means, medians and p10/p90 come from the warm steps; cold_cache
-repeats --cold-steps steps after a 512 MiB fill that evicts L2 and the
-memory-side cache before each one; graph times --graph-steps replays of
-select + attend captured once in a HIP graph.
+repeats --cold-steps steps after a 512 MiB read that evicts L2 and the
+memory-side cache before each one (and, under after_write_flush, after a
+512 MiB fill instead, whose dirty lines are written back during the step);
+graph times --graph-steps replays of select + attend captured once in a HIP
+graph.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                   [--no-workloads] [--cold-steps N] [--graph-steps N]
@@ -379,25 +381,36 @@ def main():
     att_ms = [e[1].elapsed_time(e[2]) for e in evs]
     both_ms = [e[0].elapsed_time(e[2]) for e in evs]
 
-    # Cold caches: before each of these steps a fill kernel writes 512 MiB,
-    # which evicts every XCD's L2 and the memory-side cache; the flush is
-    # outside the timed event pairs.
+    # Cold caches: before each of these steps a 512 MiB buffer is read (a
+    # reduction), which evicts every XCD's L2 and the memory-side cache and
+    # leaves them holding clean lines; the flush is outside the timed event
+    # pairs.  A second pass flushes by writing the 512 MiB instead (a fill
+    # kernel), which leaves the caches full of dirty lines that are written
+    # back while the step runs.
     cold = None
     if args.cold_steps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_steps)]
-        for i in range(args.cold_steps):
-            flush.fill_(i & 0xFF)
-            step(cevs[i])
-        torch.cuda.synchronize()
-        del flush
-        cold = {
-            "steps": args.cold_steps,
-            "flush_bytes": 512 << 20,
-            "select_ms_median": float(np.median([e[0].elapsed_time(e[1]) for e in cevs])),
-            "attend_ms_median": float(np.median([e[1].elapsed_time(e[2]) for e in cevs])),
-            "select_attend_ms_median": float(np.median([e[0].elapsed_time(e[2]) for e in cevs])),
-        }
+        flush.fill_(1)
+        sink = torch.empty((), dtype=torch.int64, device=dev)
+
+        def cold_pass(write):
+            cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_steps)]
+            for i in range(args.cold_steps):
+                if write:
+                    flush.fill_(i & 0xFF)
+                else:
+                    torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
+                step(cevs[i])
+            torch.cuda.synchronize()
+            return {
+                "select_ms_median": float(np.median([e[0].elapsed_time(e[1]) for e in cevs])),
+                "attend_ms_median": float(np.median([e[1].elapsed_time(e[2]) for e in cevs])),
+                "select_attend_ms_median": float(np.median([e[0].elapsed_time(e[2]) for e in cevs])),
+            }
+        cold = {"steps": args.cold_steps, "flush_bytes": 512 << 20, "flush": "read"}
+        cold.update(cold_pass(False))
+        cold["after_write_flush"] = cold_pass(True)
+        del flush, sink
     # The same select + attend captured once in a HIP graph and replayed:
     # the step a serving loop would launch, without per-kernel launch calls.
     graph = None
