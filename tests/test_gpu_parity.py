@@ -7,11 +7,9 @@ Select: row_ptr bit-exact; pooled scores within 1e-12 of the row scale
 Attend: bf16 output within max |err| <= 1e-2 and cosine >= 0.9999 of the
 oracle run on the GPU's own mask; LSE within 2e-3.  Small grids, the stream
 chunk and both 768-line first chunks are compared element by element on the
-whole tensor (the oracle spread over heads on worker processes); at the 4K
-chunk, every row the launch splits over several workgroups plus 768 rows
-(every head's corner and edge blocks, the rest at random) are compared."""
+whole tensor (the oracle spread over heads on worker processes), and so is
+the 184320-token 4K chunk (6.5 TFLOP of float64 oracle attention)."""
 import math
-import zlib
 
 import numpy as np
 import pytest
@@ -122,10 +120,10 @@ def split_tail_rows(plan):
     return out
 
 
-@pytest.mark.parametrize("name", ["first_768x1280", "first_768x1408"])
+@pytest.mark.parametrize("name", ["first_768x1280", "first_768x1408", "first_2048x3840"])
 def test_attend_parity_whole_tensor(name):
-    """Every row of the 768-line first chunks against the oracle (run over
-    the GPU's own mask), including the rows of the split tail."""
+    """Every row of the first chunks against the oracle (run over the GPU's
+    own mask), including the rows of the split tail."""
     desc, q, k, v = device_qkv(name)
     plan = lcsa.Plan.from_desc(desc)
     rp, ci = lcsa.select(plan, q, k)
@@ -159,55 +157,6 @@ def test_attend_parity_whole_tensor(name):
             sel[bb, oracle.block_tokens(g, qb), h] = True
         compare_output(o_h[sel], o_ref[sel], f"{name} split-tail rows")
     lerr = float(np.abs(lse.cpu().numpy() - lse_ref).max())
-    say(f"  LSE max|err| {lerr:.3e}")
-    assert lerr <= LSE_TOL
-
-
-def _stratified_rows(g, n_random, seed):
-    """Every head's blocks at the frame's corners and edges (first and last
-    block row and column) of the first and last query frame, plus n_random
-    other rows."""
-    rows = set()
-    edge = [p for p in range(g.nbf)
-            if p // g.nbw in (0, g.nbh - 1) or p % g.nbw in (0, g.nbw - 1)]
-    rng = np.random.default_rng(seed)
-    for bh in range(g.batch * g.heads):
-        for tq in sorted({0, g.q_frames - 1}):
-            for p in rng.choice(edge, size=min(6, len(edge)), replace=False):
-                rows.add(bh * g.nqb + tq * g.nbf + int(p))
-    total = g.batch * g.heads * g.nqb
-    rest = [r for r in rng.choice(total, size=min(total, n_random + len(rows)), replace=False)
-            if r not in rows]
-    rows.update(int(r) for r in rest[:n_random])
-    rows.update([0, total - 1])
-    return sorted(rows)
-
-
-def test_attend_parity_sampled_4k():
-    name = "first_2048x3840"
-    desc, q, k, v = device_qkv(name)
-    plan = lcsa.Plan.from_desc(desc)
-    rp, ci = lcsa.select(plan, q, k)
-    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
-    torch.cuda.synchronize()
-    _, inp = host_inputs(name)
-    g = oracle.geometry(desc)
-    split = split_tail_rows(plan)
-    rows = sorted(set(_stratified_rows(g, 768, seed=zlib.crc32(name.encode()))) | set(split))
-    say(f"  {name}: {len(rows)} rows compared ({len(split)} split-tail rows on this GPU)")
-    assert len(rows) >= 768
-    rp_h = rp.cpu().numpy().astype(np.int64)
-    ci_h = ci.cpu().numpy().astype(np.int64)
-    with OraclePool(desc, inp.q, inp.k, inp.v) as pool:
-        ref = pool.attend_rows(rp_h, ci_h, rows)
-    o_h = bf16_to_np(o)
-    lse_h = lse.cpu().numpy()
-    got, want, lerr = [], [], 0.0
-    for b, h, qtok, orow, lrow in ref:
-        got.append(o_h[b, qtok, h, :])
-        want.append(orow)
-        lerr = max(lerr, float(np.abs(lse_h[b, h, qtok] - lrow).max()))
-    compare_output(np.stack(got), np.stack(want), f"{name} ({len(rows)} sampled rows)")
     say(f"  LSE max|err| {lerr:.3e}")
     assert lerr <= LSE_TOL
 
