@@ -84,13 +84,6 @@ def test_attend_parity_full(name):
     assert lerr <= LSE_TOL
 
 
-def _sample_rows(rows, n, seed):
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(rows, size=min(n, rows), replace=False).tolist())
-    pick.update([0, rows - 1])
-    return sorted(pick)
-
-
 def split_tail_rows(plan):
     """CSR rows that lcsa_attend (with its workspace) splits over several
     workgroups on this GPU: the rows % slots last rows of the launch's
