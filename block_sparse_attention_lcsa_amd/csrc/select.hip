@@ -237,13 +237,41 @@ __device__ inline int window_kb(const GridGeom& g, const WindowBox& w, int e) {
 // The wave's cross-lane operations for the top-k of topk_wave.h.
 struct DeviceWave {
   __device__ uint64_t ballot(bool pred) const { return __builtin_amdgcn_ballot_w64(pred); }
-  // wave-wide OR and AND of a 64-bit value
+  // Wave-wide OR and AND of a 64-bit value, returned in scalar registers:
+  // DPP moves combine each 16-lane row (swap within pairs, within quads,
+  // then rotate the row by 4 and by 8), and the four rows' results are read
+  // from lanes 0, 16, 32 and 48.  Needs every lane active.
+  template <int CTRL>
+  __device__ static uint32_t dpp(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  }
+  __device__ static uint32_t row_or(uint32_t x) {
+    x |= dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+    x |= dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    x |= dpp<0x124>(x);   // row_ror:4
+    x |= dpp<0x128>(x);   // row_ror:8
+    return x;
+  }
+  __device__ static uint32_t row_and(uint32_t x) {
+    x &= dpp<0xB1>(x);
+    x &= dpp<0x4E>(x);
+    x &= dpp<0x124>(x);
+    x &= dpp<0x128>(x);
+    return x;
+  }
+  __device__ static uint32_t rows_or(uint32_t x) {
+    return __builtin_amdgcn_readlane(x, 0) | __builtin_amdgcn_readlane(x, 16) |
+           __builtin_amdgcn_readlane(x, 32) | __builtin_amdgcn_readlane(x, 48);
+  }
+  __device__ static uint32_t rows_and(uint32_t x) {
+    return __builtin_amdgcn_readlane(x, 0) & __builtin_amdgcn_readlane(x, 16) &
+           __builtin_amdgcn_readlane(x, 32) & __builtin_amdgcn_readlane(x, 48);
+  }
   __device__ void or_and(uint64_t& o, uint64_t& a) const {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      o |= (uint64_t)__shfl_xor((unsigned long long)o, m);
-      a &= (uint64_t)__shfl_xor((unsigned long long)a, m);
-    }
+    const uint32_t olo = rows_or(row_or((uint32_t)o)), ohi = rows_or(row_or((uint32_t)(o >> 32)));
+    const uint32_t alo = rows_and(row_and((uint32_t)a)), ahi = rows_and(row_and((uint32_t)(a >> 32)));
+    o = ((uint64_t)ohi << 32) | olo;
+    a = ((uint64_t)ahi << 32) | alo;
   }
 };
 
@@ -446,7 +474,7 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
     lt += __shfl_xor(lt, m);
     all += __shfl_xor(all, m);
   }
-  const int keep = min(g.k, w.n);
+  const int keep = __builtin_amdgcn_readfirstlane(min(g.k, w.n));
   const uint64_t below = (1ull << lane) - 1ull;
   DeviceWave dw;
   int kb[M];
