@@ -267,6 +267,16 @@ struct DeviceWave {
     return __builtin_amdgcn_readlane(x, 0) & __builtin_amdgcn_readlane(x, 16) &
            __builtin_amdgcn_readlane(x, 32) & __builtin_amdgcn_readlane(x, 48);
   }
+  // wave-wide sum of a 32-bit integer, in a scalar register
+  __device__ static int sum(int x) {
+    uint32_t v = (uint32_t)x;
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x128>(v);
+    return (int)(__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+                 __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+  }
   __device__ void or_and(uint64_t& o, uint64_t& a) const {
     const uint32_t olo = rows_or(row_or((uint32_t)o)), ohi = rows_or(row_or((uint32_t)(o >> 32)));
     const uint32_t alo = rows_and(row_and((uint32_t)a)), ahi = rows_and(row_and((uint32_t)(a >> 32)));
@@ -470,10 +480,8 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
     all += c;
     lt += q < pos ? c : 0;
   }
-  for (int m = 32; m >= 1; m >>= 1) {
-    lt += __shfl_xor(lt, m);
-    all += __shfl_xor(all, m);
-  }
+  lt = DeviceWave::sum(lt);
+  all = DeviceWave::sum(all);
   const int keep = __builtin_amdgcn_readfirstlane(min(g.k, w.n));
   const uint64_t below = (1ull << lane) - 1ull;
   DeviceWave dw;
