@@ -400,6 +400,18 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   for (int u = 0; u < kD; ++u)
 #pragma unroll
     for (int j = 0; j < MW; ++j) buf0[u][j] = kp[j][u * 8];
+  // CSR offset of these rows (worked out while the loads above are in
+  // flight): rows run (b, h, frame, position); every frame
+  // holds the same per-position counts min(k, |window(position)|).
+  int lt = 0, all = 0;
+  for (int q = p.tau ? g.nbf : lane; q < g.nbf; q += 64) {
+    const int qy = q / g.nbw, qx = q - qy * g.nbw;
+    const int c = min(g.k, window_box(g, qy, qx).n);
+    all += c;
+    lt += q < pos ? c : 0;
+  }
+  lt = DeviceWave::sum(lt);
+  all = DeviceWave::sum(all);
 #pragma unroll
   for (int u = 0; u < (int)(sizeof(qreg) / sizeof(double)); ++u) {
     const int i = tid + u * kSelectWaves * 64;
@@ -471,17 +483,6 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   __syncthreads();
   if (wave >= nr) return;
 
-  // CSR offset of these rows: rows run (b, h, frame, position); every frame
-  // holds the same per-position counts min(k, |window(position)|).
-  int lt = 0, all = 0;
-  for (int q = p.tau ? g.nbf : lane; q < g.nbf; q += 64) {
-    const int qy = q / g.nbw, qx = q - qy * g.nbw;
-    const int c = min(g.k, window_box(g, qy, qx).n);
-    all += c;
-    lt += q < pos ? c : 0;
-  }
-  lt = DeviceWave::sum(lt);
-  all = DeviceWave::sum(all);
   const int keep = __builtin_amdgcn_readfirstlane(min(g.k, w.n));
   const uint64_t below = (1ull << lane) - 1ull;
   DeviceWave dw;
