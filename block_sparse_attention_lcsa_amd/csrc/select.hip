@@ -327,11 +327,12 @@ struct ScoreShape {
 // so each pooled-key load feeds R dot products.  Top-k: wave w then takes
 // rows w, w + 4, ... and reads candidate e = lane + 64 j (j < M) of its row.
 template <int M, int R>
-__global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams p) {
+__global__ void __launch_bounds__(kSelectWaves * 64, (M <= 4 && R <= 3 ? 4 : 1)) select_kernel(SelectParams p) {
   constexpr int SW = ScoreShape<M>::waves;
   constexpr int MW = ScoreShape<M>::slots;   // scoring slots per lane
   __shared__ double qs[R][128];
   __shared__ double sc[R][64 * M];
+  __shared__ int kbs[64 * M];
   const GridGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -400,6 +401,9 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   for (int u = 0; u < kD; ++u)
 #pragma unroll
     for (int j = 0; j < MW; ++j) buf0[u][j] = kp[j][u * 8];
+  // Key block of every window candidate, for the top-k after the scoring:
+  // worked out once per workgroup while the loads above are in flight.
+  for (int e = tid; e < 64 * M; e += kSelectWaves * 64) kbs[e] = e < w.n ? window_kb(g, w, e) : 0;
   // CSR offset of these rows (worked out while the loads above are in
   // flight): rows run (b, h, frame, position); every frame
   // holds the same per-position counts min(k, |window(position)|).
@@ -492,7 +496,7 @@ __global__ void __launch_bounds__(kSelectWaves * 64) select_kernel(SelectParams 
   for (int j = 0; j < M; ++j) {
     const int e = lane + 64 * j;
     valid[j] = e < w.n;
-    kb[j] = valid[j] ? window_kb(g, w, e) : 0;
+    kb[j] = kbs[e];
   }
 
   for (int r = wave; r < nr; r += kSelectWaves) {
