@@ -32,6 +32,7 @@ graph.
   python bench.py --workload stream_768x1280 --ring   # streaming steady state
   python bench.py --rope                               # rotary embedding fused into select
   python bench.py --workload stream_768x1280 --reuse [--ring]   # steady threshold reuse
+  python bench.py --heads 3            # one GPU's share of 12 heads sharded over 4 GPUs
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
 from __future__ import annotations
@@ -216,6 +217,9 @@ def main():
     ap.add_argument("--ring", action="store_true",
                     help="K/V in a frame ring with the pooled-K cache: each step pools only "
                          "the chunk's q_frames new frames (streaming steady state)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="heads of the timed workload (0: its own, 12 for the named chunks); "
+                         "e.g. 3 = one GPU's share when the 12 heads are sharded over 4 GPUs")
     ap.add_argument("--reuse", action="store_true",
                     help="steady threshold reuse (lcsa_select_reuse): each step selects by the "
                          "previous chunk's per-row thresholds (from lcsa_select_steady) instead "
@@ -238,6 +242,11 @@ def main():
 
     name = args.workload
     desc = dict(li.CONFIGS[name])
+    if args.heads < 0:
+        print("bench.py: --heads must be positive", file=sys.stderr)
+        sys.exit(2)
+    if args.heads:
+        desc["heads"] = args.heads
     inp = li.generate(desc, seed=args.seed)
     dev = torch.device("cuda:0")
 
@@ -587,7 +596,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": _traffic(name),
+            "traffic": _traffic(name) if desc["heads"] == li.CONFIGS[name]["heads"] else None,
         },
         "select_roofline": {
             "bound": "hbm",
