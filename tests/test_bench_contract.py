@@ -20,6 +20,14 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
+def test_negative_head_count_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--heads", "-1"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--heads" in r.stderr
+    assert r.stdout.strip() == ""
+
+
 def test_traffic_record_keyed_by_kernel_source(tmp_path, monkeypatch):
     src = tmp_path / "attend.hip"
     src.write_text("kernel v1\n")
