@@ -31,17 +31,19 @@ def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 @functools.lru_cache(maxsize=2)
-def host_inputs(name: str, seed: int = 0, batch: int | None = None):
+def host_inputs(name: str, seed: int = 0, batch: int | None = None, heads: int | None = None):
     desc = dict(li.CONFIGS[name])
     if batch is not None:
         desc["batch"] = batch
+    if heads is not None:
+        desc["heads"] = heads
     inp = li.generate(desc, seed=seed)
     return desc, inp
 
 
 @functools.lru_cache(maxsize=2)
-def oracle_select(name: str, seed: int = 0, batch: int | None = None):
-    desc, inp = host_inputs(name, seed, batch)
+def oracle_select(name: str, seed: int = 0, batch: int | None = None, heads: int | None = None):
+    desc, inp = host_inputs(name, seed, batch, heads)
     g = oracle.geometry(desc)
     q = li.bf16_bits_to_f64(inp.q)
     k = li.bf16_bits_to_f64(inp.k)
@@ -49,8 +51,8 @@ def oracle_select(name: str, seed: int = 0, batch: int | None = None):
     return g, rp, ci, s
 
 
-def device_qkv(name: str, seed: int = 0, batch: int | None = None):
-    desc, inp = host_inputs(name, seed, batch)
+def device_qkv(name: str, seed: int = 0, batch: int | None = None, heads: int | None = None):
+    desc, inp = host_inputs(name, seed, batch, heads)
     return desc, to_device_bf16(inp.q), to_device_bf16(inp.k), to_device_bf16(inp.v)
 
 

@@ -154,6 +154,43 @@ def test_attend_parity_whole_tensor(name):
     assert lerr <= LSE_TOL
 
 
+def test_one_gpu_head_share():
+    """One GPU's share when the 12 heads of the first 768x1280 chunk are
+    sharded over 4 GPUs: 3 heads at the full token shape.  Masks against the
+    oracle, and attention on every row against it, split and unsplit.  On a
+    256-CU GPU its 540 rows leave a last, partly filled round of 28 rows,
+    each split into the largest number of pieces the entry point uses (16)."""
+    name, heads = "first_768x1280", 3
+    desc, q, k, v = device_qkv(name, heads=heads)
+    plan = lcsa.Plan.from_desc(desc)
+    rp, ci = lcsa.select(plan, q, k)
+    o, lse = lcsa.attend(plan, q, k, v, rp, ci, return_lse=True)
+    o1 = lcsa.attend(plan, q, k, v, rp, ci, split_tail=False)
+    torch.cuda.synchronize()
+    g, rp_ref, ci_ref, s_ref = oracle_select(name, heads=heads)
+    mism, ties = check_mask(g, rp_ref, ci_ref, s_ref, rp.cpu().numpy(), ci.cpu().numpy())
+    split = split_tail_rows(plan)
+    say(f"  {heads}-head share: rows {plan.info['rows']}, mask mismatches {len(mism)} "
+        f"(near-ties {len(ties)}), {len(split)} split-tail rows")
+    _, inp = host_inputs(name, heads=heads)
+    with OraclePool(desc, inp.q, inp.k, inp.v) as pool:
+        o_ref, lse_ref, _ = pool.attend(rp.cpu().numpy().astype(np.int64),
+                                        ci.cpu().numpy().astype(np.int64))
+    o_h = bf16_to_np(o)
+    compare_output(o_h, o_ref, f"{heads}-head share whole tensor")
+    compare_output(bf16_to_np(o1), o_ref, f"{heads}-head share, no split")
+    if split:
+        sel = np.zeros((g.batch, g.q_tokens, g.heads), dtype=bool)
+        for r in split:
+            bb, rem = divmod(r, g.heads * g.nqb)
+            h, qb = divmod(rem, g.nqb)
+            sel[bb, oracle.block_tokens(g, qb), h] = True
+        compare_output(o_h[sel], o_ref[sel], f"{heads}-head share split-tail rows")
+    lerr = float(np.abs(lse.cpu().numpy() - lse_ref).max())
+    say(f"  LSE max|err| {lerr:.3e}")
+    assert lerr <= LSE_TOL
+
+
 @pytest.mark.parametrize("name", ["tiny_window", "small_edges", "stream_768x1280",
                                   "first_768x1280"])
 def test_attend_split_tail_matches_unsplit(name):
