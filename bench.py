@@ -20,7 +20,8 @@ cpu_baseline = the float64 CPU oracle on the same step, its heads spread
 over worker processes (1 warm-up and 3 timed runs, medians); parity = the
 GPU's CSR, O and LSE of that step against the oracle's, on every row and
 element; workloads = select and attend medians of the other named workloads
-in the same run.  Means, medians and p10/p90 come from the warm steps; cold_cache
+in the same run, each with the oracle's host timing and a parity record of
+its own.  Means, medians and p10/p90 come from the warm steps; cold_cache
 repeats --cold-steps steps after a 512 MiB read that evicts L2 and the
 memory-side cache before each one (and, under after_write_flush, after a
 512 MiB fill instead, whose dirty lines are written back during the step);
@@ -622,16 +623,19 @@ def main():
         del q, k, v, out, att_ws, ws
         torch.cuda.empty_cache()
         res["workloads"] = time_workloads([n for n in li.PAGE_WORKLOADS if n != name],
-                                          args.seed, dev, stream)
+                                          args.seed, dev, stream, cpu=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 
-def time_workloads(names, seed, dev, stream):
+def time_workloads(names, seed, dev, stream, cpu=True):
     """Step time and select / attend medians of the other named workloads,
     timed with HIP events on the launch stream in this same run: a spin-up
     of SPIN_UP_S seconds and 10 warm-up steps, then 50 steps back to back (20
     at the 184320-token chunk) for the step time, then as many with events
-    around select and attend (medians, p10 and p90)."""
+    around select and attend (medians, p10 and p90).  With `cpu`, each
+    workload also gets the oracle timed on the host cores (as cpu_baseline:
+    1 warm-up and 3 timed runs, 1 at the 184320-token chunk) and a parity
+    record of one more GPU step against it on every row and element."""
     import numpy as np
     import torch
     import block_sparse_attention_lcsa_amd as lcsa
@@ -706,6 +710,26 @@ def time_workloads(names, seed, dev, stream):
             "step_tflops": flops / (step_ms * 1e-3) / 1e12,
         }
         print(f"bench: {name} select {sel:.4f} ms, attend {att:.4f} ms", file=sys.stderr, flush=True)
+        if cpu:
+            # the oracle on the host cores, and the parity of one more GPU step
+            rp_g, ci_g = lcsa.select(plan, q, k, workspace=ws)
+            o_g, lse_g = lcsa.attend(plan, q, k, v, rp_g, ci_g, return_lse=True, workspace=att_ws)
+            torch.cuda.synchronize()
+            gpu = (rp_g.cpu().numpy().astype(np.int64), ci_g.cpu().numpy().astype(np.int64),
+                   o_g.float().cpu().numpy(), lse_g.cpu().numpy())
+            del rp_g, ci_g, o_g, lse_g
+            base, par = cpu_baseline(name, desc, inp, flops, gpu,
+                                     runs=1 if info["q_tokens"] > 100000 else 3)
+            del gpu
+            out[name]["cpu_oracle"] = {key: base[key] for key in (
+                "value", "unit", "ms_per_step", "select_s_median", "attend_s_median",
+                "processes", "sample")}
+            out[name]["parity"] = {key: par[key] for key in (
+                "rows", "mask_rows_differing", "mask_near_ties", "mask_mismatches_not_near_tie",
+                "attend_elements", "attend_max_abs_err", "attend_cosine",
+                "attend_worst_head_cosine", "lse_max_abs_err", "pass")}
+            print(f"bench: {name} oracle {base['ms_per_step'] / 1e3:.2f} s per step, parity "
+                  f"{'pass' if par['pass'] else 'FAIL'}", file=sys.stderr, flush=True)
         del q, k, v, o, ws, att_ws, inp
         torch.cuda.empty_cache()
     return out
