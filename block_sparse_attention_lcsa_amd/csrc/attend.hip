@@ -33,10 +33,12 @@
 //    the row sum rescaled and P recomputed.  O and the row sum share the
 //    reference, so the result is unchanged; P <= 2^16 keeps sums finite.
 //  * Rows are visited head by head, in square tiles of block positions with
-//    all query frames of a tile together, and each XCD (workgroup id mod 8)
-//    walks a contiguous range of that order: the rows in flight on an XCD
-//    have overlapping windows and select largely the same key blocks, which
-//    then stay in that XCD's L2 and the memory-side cache.
+//    all query frames of a tile together.  The order is dealt to the XCDs
+//    (workgroup id mod 8) in chunks of one XCD's resident workgroups, round
+//    robin: the rows in flight on an XCD have overlapping windows and select
+//    largely the same key blocks, which stay in that XCD's L2, and the eight
+//    XCDs work on neighbouring chunks of one head, whose K/V then stay in the
+//    memory-side cache.
 
 #include <hip/hip_runtime.h>
 
@@ -180,9 +182,10 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
   const int half = lane >> 5, l32 = lane & 31;
 
   // Work item: workgroups [0, full_rows) take whole rows, in an XCD-aware
-  // order (workgroup ids go round-robin over the XCDs; XCD x gets the
-  // contiguous range [start_x, start_x + count_x) of the visiting order);
-  // later workgroups take piece `piece` of a split row.
+  // order (workgroup ids go round-robin over the XCDs; XCD x takes chunks
+  // x, x + 8, x + 16, ... of xcd_chunk rows of the visiting order, and the
+  // rows past the last whole round of 8 chunks in plain order); later
+  // workgroups take piece `piece` of a split row.
   // With a row order, workgroup i takes row order[i]: the order is meant to
   // be dispatched as it stands (longest rows first), round-robin over the
   // XCDs.
@@ -194,9 +197,13 @@ __global__ void __launch_bounds__(BT * 2, 2) attend_fwd_kernel(AttendParams p) {
       if (p.order) {
         row = pid;
       } else {
-        const int64_t xcd = pid % kXcds, idx = pid / kXcds;
-        const int64_t per = n / kXcds, rem = n % kXcds;
-        row = xcd * per + (xcd < rem ? xcd : rem) + idx;
+        const int64_t c = p.xcd_chunk, whole = n / (kXcds * c) * (kXcds * c);
+        if (pid < whole) {
+          const int64_t xcd = pid % kXcds, idx = pid / kXcds;
+          row = ((idx / c) * kXcds + xcd) * c + idx % c;
+        } else {
+          row = pid;
+        }
       }
     } else {
       item = pid - n;

@@ -317,6 +317,7 @@ lcsa_status attend_impl(const char* fn, const lcsa_plan_s* plan, const lcsa_tens
   ap.full_rows = full_rows;
   ap.pieces = pieces;
   ap.tile = attend_tile(slots, plan->desc.q_frames, in.nbh, in.nbw);
+  ap.xcd_chunk = static_cast<int32_t>(slots / 8 > 0 ? slots / 8 : 1);
   ap.part = static_cast<float*>(d_workspace);
   ap.scale_log2 = static_cast<float>(in.scale * 1.4426950408889634);
   ap.order = nullptr;

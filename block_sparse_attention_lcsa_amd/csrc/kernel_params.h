@@ -95,6 +95,9 @@ struct AttendParams {
   // tile of tile x tile block positions, query frame, position in the tile);
   // work items above are enumeration indices.
   int32_t tile;
+  // Rows per XCD chunk of the whole-row workgroups (>= 1): one XCD's
+  // resident workgroups.
+  int32_t xcd_chunk;
   float* part;           // [items][BT][128] partial O, then [items][BT][2] (m, l)
   float scale_log2;      // softmax scale * log2(e)
   // Optional order of the rows (a permutation of [0, rows)): workgroup i
